@@ -1,0 +1,69 @@
+"""Seeded synthetic inputs for the verify step.
+
+This module only draws random numbers; it holds none of the step's
+arithmetic.  It is the one piece shared by the tests, the bench and the CPU
+oracle's callers: inputs are drawn here on the host, then handed to both the
+device library and the oracle.
+
+Recipe (per workload w and tensor id t: h=0, W=1, LM=2, Kc=3, Vc=4, Q=5):
+  * a torch CPU generator seeded with ``seed_of(w, t, chunk)``;
+  * float32 normal draws; W and LM scaled by 0.02 (standard deviation), the
+    rest standard normal;
+  * bf16 workloads round the float32 draws to bf16 (round to nearest even).
+Large tensors are drawn in chunks along the leading dimension so host memory
+stays bounded.
+"""
+
+import torch
+
+TENSOR_IDS = {"h": 0, "W": 1, "LM": 2, "Kc": 3, "Vc": 4, "Q": 5}
+WEIGHT_STD = 0.02
+
+
+def seed_of(workload, tensor_id, chunk=0):
+    """Deterministic 63-bit seed for (workload, tensor, chunk)."""
+    s = 2026
+    for v in (workload, tensor_id, chunk):
+        s = (s * 1_000_003 + v + 1) % (1 << 63)
+    return s
+
+
+def normal(shape, seed, std=1.0, dtype="f32"):
+    """N(0, std^2) float32 draws, optionally rounded to bf16, as a CPU tensor."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def _chunked(shape, workload, name, std, dtype):
+    tid = TENSOR_IDS[name]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty(*shape, dtype=tdt)
+    lead = shape[0]
+    for c in range(lead):
+        out[c] = normal(shape[1:], seed_of(workload, tid, c), std, dtype)
+    return out
+
+
+def make_inputs(cfg, names=("h", "W", "LM", "Kc", "Vc", "Q")):
+    """Host tensors for one workload (torch CPU tensors, fp32 or bf16).
+
+    h [b, H]; W [K, H, H] ([head, out, in]); LM [V, H];
+    Kc, Vc [b, nkv, Pmax, d] with the tree nodes' K/V at slots P..P+T-1;
+    Q [b, T, nq, d] (the tree nodes' queries).
+    """
+    shapes = {
+        "h": (cfg.b, cfg.H),
+        "W": (cfg.K, cfg.H, cfg.H),
+        "LM": (cfg.V, cfg.H),
+        "Kc": (cfg.b, cfg.nkv, cfg.Pmax, cfg.d),
+        "Vc": (cfg.b, cfg.nkv, cfg.Pmax, cfg.d),
+        "Q": (cfg.b, cfg.T, cfg.nq, cfg.d),
+    }
+    out = {}
+    for n in names:
+        std = WEIGHT_STD if n in ("W", "LM") else 1.0
+        out[n] = _chunked(shapes[n], cfg.index, n, std, cfg.dtype)
+    return out

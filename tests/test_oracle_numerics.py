@@ -1,0 +1,189 @@
+"""Pins for the oracle's heads, bf16 rounding, top-k and sampler.
+
+Heads: aicassindra.com "Medusa deep dive", "The heads are residual blocks":
+head_i(h) = LMproj(h + SiLU(W_i h)); a zero W_i leaves the plain projection.
+The checks use routines the oracle does not use (pure-Python loops, torch's
+linear/silu, torch's bf16 conversion, torch.topk) and published values.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (heads, lm_project, round_bf16, topk_stable, argmax_lowest,
+                    splitmix64, counter_uniform, sample_tempered)
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+# ---------------------------------------------------------------- heads
+@pytest.mark.parametrize("bf16", [False, True])
+def test_zero_head_is_plain_projection(bf16):
+    h = round_bf16(_rand((3, 32), 1))
+    LM = round_bf16(_rand((50, 32), 2, 0.02))
+    W = np.zeros((4, 32, 32))
+    u, logits = heads(h, W, LM, bf16)
+    for i in range(5):
+        assert np.array_equal(u[:, i], h)                       # SiLU(0) = 0
+        assert np.allclose(logits[:, i], h @ LM.T, rtol=0, atol=1e-13)
+
+
+def test_heads_against_python_loops():
+    b, H, V, K = 2, 6, 9, 2
+    h = _rand((b, H), 3)
+    W = _rand((K, H, H), 4)          # not symmetric: a transposed W would fail
+    LM = _rand((V, H), 5)
+    u, logits = heads(h, W, LM, bf16=False)
+    for s in range(b):
+        for i in range(K):
+            for o in range(H):
+                z = sum(W[i][o][j] * h[s][j] for j in range(H))
+                want = h[s][o] + z / (1.0 + math.exp(-z))
+                assert abs(u[s, i + 1, o] - want) < 1e-12
+        for i in range(K + 1):
+            for v in range(V):
+                want = sum(LM[v][j] * u[s, i, j] for j in range(H))
+                assert abs(logits[s, i, v] - want) < 1e-12
+
+
+def test_heads_against_torch_fp64():
+    b, H, V, K = 4, 48, 70, 3
+    h, W, LM = _rand((b, H), 6), _rand((K, H, H), 7, 0.2), _rand((V, H), 8, 0.1)
+    u, logits = heads(h, W, LM, bf16=False)
+    th = torch.from_numpy(h)
+    for i in range(K):
+        ref = th + torch.nn.functional.silu(torch.nn.functional.linear(th, torch.from_numpy(W[i])))
+        assert np.allclose(u[:, i + 1], ref.numpy(), rtol=1e-13, atol=1e-13)
+    ref_logits = torch.nn.functional.linear(torch.from_numpy(u), torch.from_numpy(LM))
+    assert np.allclose(logits, ref_logits.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_lm_project_orientation():
+    x = np.array([[1.0, 0.0, 0.0]])
+    LM = np.array([[2.0, 3.0, 5.0], [7.0, 11.0, 13.0]])
+    assert lm_project(x, LM).tolist() == [[2.0, 7.0]]
+
+
+# ---------------------------------------------------------------- bf16
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, -2.5, 65504.0, 1e-30]])
+    x32 = x.astype(np.float32)
+    # exact halfway cases: low 16 bits = 0x8000, even and odd upper halves
+    halves = (np.arange(1000, dtype=np.uint32) << 16 | 0x8000) + (0x3F80 << 16)
+    x32 = np.concatenate([x32, halves.view(np.float32)])
+    ours = round_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------- top-k
+def _brute_topk(row, k):
+    chosen = []
+    for _ in range(k):
+        best = None
+        for i, v in enumerate(row):
+            if i in chosen:
+                continue
+            if best is None or v > row[best]:     # strict: first (lowest) index wins ties
+                best = i
+        chosen.append(best)
+    return chosen
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(10)
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        row = rng.integers(-3, 4, n).astype(np.float64)     # many ties
+        k = int(rng.integers(1, n + 1))
+        assert list(topk_stable(row, k)) == _brute_topk(list(row), k)
+        assert argmax_lowest(row) == _brute_topk(list(row), 1)[0]
+
+
+def test_topk_matches_torch_on_distinct_values():
+    row = np.random.default_rng(11).standard_normal(5000)
+    idx = topk_stable(row, 16)
+    ref = torch.topk(torch.from_numpy(row), 16).indices.numpy()
+    assert list(idx) == list(ref)
+
+
+def test_signed_zero_is_a_tie():
+    row = np.array([-0.0, 0.0, -1.0, -0.0])
+    assert list(topk_stable(row, 3)) == [0, 1, 3]
+
+
+# ---------------------------------------------------------------- sampler
+def test_splitmix64_published_values():
+    with open(os.path.join(GOLD, "splitmix64_state0.txt")) as f:
+        want = [int(ln, 16) for ln in f if ln.strip() and not ln.startswith("#")]
+    state, got = 0, []
+    for _ in want:
+        got.append(splitmix64(state))
+        state = (state + 0x9E3779B97F4A7C15) % (1 << 64)
+    assert got == want
+
+
+def test_counter_uniform_range_and_resolution():
+    us = [counter_uniform(0x5EED, s, q, d) for s in range(20) for q in range(8) for d in (0, 1)]
+    assert all(0.0 <= u < 1.0 for u in us)
+    assert all(float(u * 2 ** 24).is_integer() for u in us)
+    assert len(set(us)) == len(us)
+    # counter fields do not alias: draw, seq and step each change the value
+    assert counter_uniform(1, 0, 0, 0) != counter_uniform(1, 0, 0, 1)
+    assert counter_uniform(1, 0, 0, 0) != counter_uniform(1, 0, 1, 0)
+    assert counter_uniform(1, 0, 0, 0) != counter_uniform(1, 1, 0, 0)
+
+
+def test_sampler_inverse_cdf_by_linear_scan():
+    rng = np.random.default_rng(12)
+    for _ in range(100):
+        n = int(rng.integers(1, 30))
+        row = rng.standard_normal(n) * 3
+        T = float(np.float32(rng.uniform(0.3, 2.0)))
+        u = float(rng.integers(0, 2 ** 24)) * 2.0 ** -24
+        m = max(row)
+        w = [math.exp((x - m) / T) for x in row]
+        target = u * sum(w)
+        acc, want = 0.0, n - 1
+        for i, wi in enumerate(w):
+            acc += wi
+            if acc > target:
+                want = i
+                break
+        got, c = sample_tempered(row, T, u)
+        margin = min(abs(ci - target) for ci in c) / c[-1]
+        if margin > 1e-12:
+            assert got == want
+
+
+def test_sampler_frequencies_on_a_uniform_grid():
+    # A deterministic grid of u values lands in index i exactly ~n*q_i times.
+    row = np.array([0.5, -1.0, 2.0, 0.0, 1.0])
+    T = 0.7
+    q = np.exp(row / T) / np.exp(row / T).sum()
+    n = 100000
+    counts = np.zeros(row.size)
+    for j in range(n):
+        counts[sample_tempered(row, T, (j + 0.5) / n)[0]] += 1
+    assert np.all(np.abs(counts - n * q) <= 1.0)
+
+
+def test_sampler_peaked_and_edges():
+    row = np.array([0.0, 50.0, 1.0])
+    for u in (2.0 ** -24, 0.5, 1.0 - 2.0 ** -24):
+        assert sample_tempered(row, 0.7, u)[0] == 1
+    # u = 0 takes the first index with any mass at all (a running sum > 0)
+    assert sample_tempered(row, 0.7, 0.0)[0] == 0
+    row = np.zeros(8)
+    assert sample_tempered(row, 1.0, 0.0)[0] == 0
+    assert sample_tempered(row, 1.0, 1.0 - 2.0 ** -24)[0] == 7
+    assert sample_tempered(row, 1.0, 0.5)[0] == 4        # running sum 5 > 4
