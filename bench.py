@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of one Medusa draft-and-verify step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+heads + LM projection, shortlists, tree, tree attention, verify logits,
+acceptance, KV compaction (seven library calls, see speculative_decoding_heads_amd/step.py).
+Default workload: the Llama-7B shape at batch 1 (hidden 4096, vocab 32000,
+4 heads, 64-candidate tree, 32 heads x 128, prefix 2048, bf16, greedy); the
+batch-16 typical-acceptance variant is measured too and reported alongside.
+
+Timing: inputs are resident in HBM; W warmup steps, then K timed steps between
+two events on the launch stream (synchronised on both sides).  Each step uses
+its own seq_len buffer (preset to P), so no reset work runs inside the timed
+region.  When a workload's weights+cache are small enough to sit in the
+256 MB Infinity Cache across steps, two copies of every input are rotated.
+A second pass of K steps records events between the calls for the per-call
+breakdown and the roofline of the dominant kernel.
+
+Prints ONE JSON line (rank 0).  --gpus N > 1 exits with a message: this build
+runs on one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Medusa verify steps/sec at 7B shape (bs1, bs16) + % of HBM/MFMA roofline"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CALLS = ["draft_heads", "topk", "build_tree", "tree_attn", "verify_lm", "accept", "kv_compact"]
+
+
+def alg_bytes(c):
+    """Algorithmic bytes each call must move (inputs read once, outputs written once)."""
+    e = 2 if c.dtype == "bf16" else 4
+    rows_d = c.b * (c.K + 1)
+    rows_v = c.b * c.T
+    return {
+        "draft_heads": c.K * c.H * c.H * e + c.V * c.H * e + c.b * c.H * e
+        + 2 * rows_d * c.H * e + rows_d * c.V * 4,
+        "topk": rows_d * c.V * 4,
+        "build_tree": c.b * c.T * 8 + c.b * c.K * c.kmax * 4,
+        "tree_attn": 2 * c.b * c.nkv * (c.P + c.T) * c.d * e + 2 * c.b * c.T * c.nq * c.d * e,
+        "verify_lm": c.V * c.H * e + rows_v * c.H * e + rows_v * c.V * 4,
+        "accept": rows_v * c.V * 4,
+        "kv_compact": 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
+    }
+
+
+def alg_flops(c):
+    return {
+        "draft_heads": 2 * c.b * c.K * c.H * c.H + 2 * c.b * (c.K + 1) * c.H * c.V,
+        "tree_attn": 4 * c.b * c.nq * c.T * (c.P + c.T) * c.d,
+        "verify_lm": 2 * c.b * c.T * c.H * c.V,
+    }
+
+
+def _enqueue(st, x, step, M, c, ev=None):
+    """The seven calls of VerifyStep.run, with optional events between them."""
+    def mark(i):
+        if ev is not None:
+            ev[i].record()
+    mark(0)
+    M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
+    mark(1)
+    M.medusa_topk(st.logits, c.k, c.kmax, st.mode, c.temperature, c.seed, step, st.root, st.idx,
+                  st.val, st.ws_topk)
+    mark(2)
+    M.medusa_build_tree(c.k, c.N, c.decay.numerator, c.decay.denominator, st.root, st.idx,
+                        x["seq_len"], st.tokens, st.pos, st.parent, st.depth, st.anc)
+    mark(3)
+    M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
+    mark(4)
+    M.medusa_heads(st.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
+                   st.base_logits.view(c.b * c.T, c.V), include_base=1)
+    mark(5)
+    M.medusa_accept(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode, c.temperature,
+                    c.eps, c.delta, c.seed, step, st.L, st.path, st.acc_tokens, st.bonus,
+                    st.ws_acc)
+    mark(6)
+    M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], st.path, st.L)
+    mark(7)
+
+
+def measure(cfg, steps, warmup, rotate=None, log=print):
+    import torch
+    from speculative_decoding_heads_amd import medusa as M
+    from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
+    from speculative_decoding_heads_amd.synth import make_inputs
+
+    M.lib()
+    c = cfg
+    t0 = time.time()
+    host = make_inputs(c)
+    ws_bytes = sum(v.numel() * v.element_size() for v in host.values())
+    if rotate is None:
+        rotate = 2 if ws_bytes < (1 << 30) else 1
+    sets = []
+    for r in range(rotate):
+        x = device_inputs(c, host)
+        sets.append(x)
+    del host
+    log(f"[bench] {c.name}: inputs {ws_bytes / 1e6:.1f} MB x {rotate} copies "
+        f"({time.time() - t0:.1f}s)")
+    st = VerifyStep(c)
+    n = warmup + 2 * steps
+    seqs = [torch.full((c.b,), c.P, dtype=torch.int32, device="cuda") for _ in range(n)]
+
+    def inputs(i):
+        x = dict(sets[i % rotate])
+        x["seq_len"] = seqs[i]
+        return x
+
+    for i in range(warmup):
+        _enqueue(st, inputs(i), i, M, c)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(warmup, warmup + steps):
+        _enqueue(st, inputs(i), i, M, c)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+
+    # per-call pass
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+    for j in range(steps):
+        i = warmup + steps + j
+        _enqueue(st, inputs(i), i, M, c, evs[j])
+    torch.cuda.synchronize()
+    per_call = {}
+    for k, name in enumerate(CALLS):
+        per_call[name] = 1000.0 * sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps   # us
+    return ms, per_call
+
+
+def cpu_baseline(cfg, seconds, log=print):
+    """The oracle (numpy float64) timed on this host on whole steps of the workload."""
+    import numpy as np
+    from oracle import oracle_step
+    from speculative_decoding_heads_amd.synth import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    c = cfg
+    host = make_inputs(c)
+    f = {k: v.float().numpy().astype(np.float64) for k, v in host.items()}
+    del host
+    P = np.full(c.b, c.P)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle_step(f["h"], f["W"], f["LM"], f["Q"], f["Kc"], f["Vc"], P, c.k, c.N, c.decay,
+                    c.mode, bf16=(c.dtype == "bf16"), temperature=c.temperature, eps=c.eps,
+                    delta=c.delta, seed=c.seed, step=done)
+        done += 1
+        el = time.perf_counter() - t0
+        log(f"[bench] oracle step {done}: {el:.1f}s")
+        if el >= seconds or done >= 20:
+            break
+    return {"value": done / el, "unit": "verify-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} full step(s) of the {c.name} workload, float64 numpy, "
+                      f"{el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama7b_bs1")
+    ap.add_argument("--also", default="llama7b_bs16",
+                    help="second workload reported alongside ('' to skip)")
+    ap.add_argument("--rotate", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs the verify step on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_heads_amd import configs as C
+
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    cfg = C.BY_NAME[args.workload]
+    ms, per_call = measure(cfg, args.steps, args.warmup, args.rotate, log)
+    value = 1000.0 / ms
+    ab, af = alg_bytes(cfg), alg_flops(cfg)
+    step_bytes = sum(ab.values())
+    dom = max(["verify_lm", "tree_attn"], key=lambda k: per_call[k])
+    t_dom = per_call[dom] * 1e-6
+    bytes_rate = ab[dom] / t_dom / 1e9
+    flop_rate = af.get(dom, 0) / t_dom / 1e12
+    ai = af.get(dom, 0) / ab[dom]
+    if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(flop_rate, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flop_rate / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_rate, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(bytes_rate / HBM_PEAK_GBPS, 4)}
+    roof.update({"kernel": dom, "alg_bytes_per_launch": ab[dom],
+                 "alg_flops_per_launch": af.get(dom, 0), "avg_launch_us": round(per_call[dom], 2),
+                 "traffic": None})
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "verify-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.b, "hidden": cfg.H, "vocab": cfg.V,
+                   "medusa_heads": cfg.K, "shortlist": list(cfg.k), "tree_candidates": cfg.N,
+                   "q_heads": cfg.nq, "kv_heads": cfg.nkv, "head_dim": cfg.d, "prefix": cfg.P,
+                   "acceptance": cfg.mode, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "step_alg_bytes": step_bytes,
+        "step_effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+    }
+    if args.also:
+        c2 = C.BY_NAME[args.also]
+        ms2, pc2 = measure(c2, args.steps, args.warmup, None, log)
+        b2 = sum(alg_bytes(c2).values())
+        out["also"] = {"workload": c2.name, "value": round(1000.0 / ms2, 2),
+                       "unit": "verify-steps/s", "ms_per_step": round(ms2, 4),
+                       "step_effective_GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
+                       "per_call_us": {k: round(v, 2) for k, v in pc2.items()}}
+    torch.cuda.synchronize()
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds, log)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * medusa.h - C ABI of libmedusa.so: one Medusa draft-and-verify step on an
+ * AMD Instinct MI355X (gfx950), in hand-written HIP kernels.
+ *
+ * Sources (web pages on Medusa heads, cited by title and section):
+ *   [deep-dive]  aicassindra.com, "Medusa deep dive" (tm_medusa_deep)
+ *   [glossary]   inferensys.com, "Medusa Heads"
+ *   [guide]      aiunderstanding.org, "Medusa Decoding Heads"
+ *   [zackli]     zackli.ai, "Speculative Decoding Deep Dive II: Medusa, MTP"
+ *
+ * Conventions for every call:
+ *   - Device pointers are caller-owned device memory (for instance a torch
+ *     tensor's data_ptr()), contiguous, row-major, in the layout given.
+ *     Pointers marked "host" are ordinary host memory, read during the call.
+ *   - A call validates its arguments on the host first; on failure it returns
+ *     a negative status, launches nothing and sets medusa_last_error().
+ *   - On success a call has only ENQUEUED its kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream) and returns MEDUSA_OK.  No call
+ *     allocates or frees device memory, synchronises, or copies device data
+ *     to the host.  A failed launch returns MEDUSA_ERR_HIP.
+ *   - Scratch memory is a caller-provided workspace `ws` of at least the
+ *     size the matching *_workspace() query returns (host-only queries).
+ *   - Floating-point inputs must be finite.  Values that only the device
+ *     sees (token ids, seq_len, L, path) are range-checked by the kernels:
+ *     an out-of-range seq_len gives NaN attention rows for that sequence and
+ *     leaves the cache untouched in compaction; out-of-range tokens are
+ *     rejected by acceptance.
+ *   - Calls are reentrant.  The only library state is an immutable cache of
+ *     tree plans keyed by (k, N, decay), guarded by a mutex.
+ *   - Calls that share buffers must be ordered on one stream by the caller.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEDUSA_ABI_VERSION 1
+
+typedef enum {
+  MEDUSA_OK = 0,
+  MEDUSA_ERR_ARG = -1,          /* invalid argument (null, range, alignment) */
+  MEDUSA_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle */
+  MEDUSA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  MEDUSA_ERR_HIP = -4           /* a HIP launch failed */
+} medusa_status;
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;   /* logits are always f32 */
+typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_mode;
+
+/* Limits of this build. */
+#define MEDUSA_MAX_HEADS 16     /* Medusa heads K */
+#define MEDUSA_MAX_K 16         /* shortlist size per head */
+#define MEDUSA_MAX_T 256        /* tree nodes including the root */
+
+int medusa_abi_version(void);
+const char* medusa_status_str(int status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* medusa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * medusa_heads - K residual Medusa heads sharing one LM projection.
+ * [deep-dive] "The heads are residual blocks, not linear layers":
+ *   head_i(h) = LMproj(h + SiLU(W_i h)),  SiLU(z) = z * sigmoid(z);
+ * [deep-dive] "What this deep dive assumes" / [zackli] "Medusa" (Head_0): the
+ * base head LMproj(h) owns t+1 and Medusa head i owns t+i+1.  The same call
+ * with n_heads = 0 is the base model's original output head applied to the
+ * verification rows ([glossary], verification phase).
+ *
+ *   x       [rows, H]            hidden states (dtype)
+ *   W       [n_heads, H, H]      head weights, [head][out][in] (dtype); NULL
+ *                                 allowed when n_heads == 0
+ *   LM      [V, H]               shared LM projection (dtype)
+ *   include_base  1: output slot 0 is the base head LMproj(x)
+ *   u_out   [rows, R, H] or NULL hidden state of every head, R =
+ *                                 include_base + n_heads: slot 0 = x (base),
+ *                                 then x + SiLU(W_i x) rounded to dtype.  NULL:
+ *                                 kept in the workspace.
+ *   logits  [rows, R, V] f32     logits[r, j, :] = LM . u[r, j, :]
+ * bf16 needs H % 128 == 0 and 16-byte aligned x, W, LM, u_out.  rows == 0 is
+ * a no-op.  Arithmetic: bf16 operands, f32 accumulation (MFMA); f32 path in
+ * f32 throughout.
+ * ------------------------------------------------------------------------- */
+size_t medusa_heads_workspace(int64_t rows, int32_t H, int32_t n_heads, int32_t include_base,
+                              int32_t dtype);
+int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t n_heads,
+                 const void* LM, int32_t V, int32_t dtype, int32_t include_base, void* u_out,
+                 float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_topk - per-head shortlists and the root token.
+ * [deep-dive] "From top-k heads to a sparse candidate tree": keep the top k_i
+ * tokens of head i.  Order: logit descending, equal logits by the lower
+ * vocabulary index (-0.0 == +0.0).
+ *
+ *   logits [b, K+1, V] f32       slot 0 = base head, slot i = Medusa head i
+ *   k_host [K] (host)            shortlist sizes, 1 <= k_i <= kmax <= 16, k_i <= V
+ *   root_mode  GREEDY: root = argmax of slot 0 (lowest index on ties).
+ *              TYPICAL: root = a sample from softmax(slot0 / temperature) in
+ *              float64: the smallest i whose running sum of
+ *              exp((x_i - max x)/T) exceeds u * (the full sum), with
+ *              u = (splitmix64(seed ^ step<<32 ^ s<<8 ^ 0) >> 40) * 2^-24
+ *              for sequence s (SplitMix64: Steele, Lea, Flood 2014).
+ *   root   [b] i32; idx [b, K, kmax] i32 (descending; -1 past k_i);
+ *   val    [b, K, kmax] f32 (the logits; -inf past k_i)
+ * ------------------------------------------------------------------------- */
+size_t medusa_topk_workspace(int32_t b, int32_t K, int32_t V, int32_t kmax);
+int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
+                int32_t kmax, int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
+                int32_t* root, int32_t* idx, float* val, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_tree_plan (host only) / medusa_build_tree - the fixed sparse tree.
+ * [deep-dive] "From top-k heads to a sparse candidate tree": the Cartesian
+ * product of shortlists is pruned ahead of time to a fixed sparse tree with
+ * more branches through confident, early heads, laid out as a flat node
+ * sequence with a matching attention mask and position ids; [zackli]
+ * "Medusa": Anc(i), and s_1 + s_1 s_2 + ... nodes for the full tree.
+ *
+ * A candidate is a rank tuple (r_1..r_D), r_d < k_d: rank r_d of head d at
+ * depth d.  The N kept candidates are the first N under (score descending,
+ * D ascending, tuple ascending), score = prod_{d=1..D} decay^d / (r_d + 1),
+ * decay = decay_num / decay_den in (0, 1), compared exactly.  N = -1 keeps
+ * all (full tree).  Node 0 is the root; then candidates by depth, tuples
+ * ascending within a depth, so parent[i] < i.  T = N + 1 <= 256.
+ *
+ * medusa_tree_plan fills host arrays parent/depth/rank [T_cap] (rank = the
+ * tuple's last rank; -1 for the root) and *T_out.
+ * medusa_build_tree, per sequence s (all device):
+ *   tokens[s, 0] = root[s];  tokens[s, i] = idx[s, depth_i - 1, rank_i]
+ *   pos[s, i]    = seq_len[s] + depth_i
+ *   parent[T], depth[T] i32; anc [T, anc_words] u64: bit (j % 64) of word
+ *   j / 64 in row i is set iff j == i or j is an ancestor of i.
+ * idx is [b, K, kmax] as written by medusa_topk.
+ * ------------------------------------------------------------------------- */
+int medusa_tree_plan(const int32_t* k_host, int32_t K, int32_t N, int32_t decay_num,
+                     int32_t decay_den, int32_t* parent, int32_t* depth, int32_t* rank,
+                     int32_t T_cap, int32_t* T_out);
+int medusa_build_tree(const int32_t* k_host, int32_t K, int32_t N, int32_t decay_num,
+                      int32_t decay_den, const int32_t* root, const int32_t* idx, int32_t b,
+                      int32_t kmax, const int32_t* seq_len, int32_t* tokens, int32_t* pos,
+                      int32_t* parent, int32_t* depth, uint64_t* anc, int32_t anc_words,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_tree_attn - one tree-masked attention layer of the verify pass.
+ * [glossary] tree attention: all branches share the prefix KV cache and all
+ * nodes are scored in one pass; [deep-dive]: a node attends only to its
+ * ancestors.  For sequence b with P = seq_len[b], node i and q head h
+ * (kv head g = floor(h * nkv / nq)):
+ *   O[b, i, h*d:(h+1)*d] = softmax_j(scale * q . k_j) v_j
+ * over j in [0, P) and the tree slots P + a, a in Anc(i) u {i}.
+ *   Q  [b, T, nq, d] (dtype)     the tree nodes' queries
+ *   Kc, Vc [b, nkv, Pmax, d]     cache; the tree nodes' K/V at slots P..P+T-1
+ *   anc [T, anc_words] u64       as written by medusa_build_tree
+ *   O  [b, T, nq*d] (dtype)
+ * Requires P + T <= Pmax per sequence (else NaN rows for that sequence),
+ * nq % nkv == 0, T <= 256; bf16: d in {64, 128}, 16-byte aligned pointers;
+ * f32: d <= 256, Pmax <= 16384.  bf16 arithmetic: MFMA products, f32 softmax,
+ * probabilities rounded to bf16 for the PV product, O rounded to bf16.
+ * ------------------------------------------------------------------------- */
+size_t medusa_tree_attn_workspace(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d,
+                                  int32_t Pmax, int32_t dtype);
+int medusa_tree_attn(const void* Q, const void* Kc, const void* Vc, const int32_t* seq_len,
+                     const uint64_t* anc, int32_t anc_words, int32_t b, int32_t T, int32_t nq,
+                     int32_t nkv, int32_t d, int32_t Pmax, float scale, int32_t dtype, void* O,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_accept - acceptance, the accepted path and the next token.
+ * [guide] "Deep Dive": accept the longest prefix matching what the model
+ * would have produced; [glossary]: stop at the first rejection, roll back,
+ * the base model gives the next token; [deep-dive] "Typical acceptance, not
+ * exact rejection sampling": accept when p(x) > min(eps, delta * exp(-H)).
+ *   base_logits [b, T, V] f32    verify logits of every node
+ *   tokens [b, T], parent [T], depth [T]   as from medusa_build_tree
+ *   GREEDY : child c of p accepted iff tokens[c] == argmax base_logits[p]
+ *            (lowest index on ties).
+ *   TYPICAL: q = softmax(base_logits[p] / temperature), H = -sum q ln q;
+ *            accepted iff q[tokens[c]] > min(eps, delta * exp(-H)).
+ *   A node is fully accepted when it and all its ancestors below the root
+ *   are.  L[b] = the largest depth of a fully accepted node (0..K); the chosen
+ *   node is the lowest node index at that depth.
+ *   path [b, K+1]       node indices root .. chosen node, -1 padded
+ *   acc_tokens [b, K+1] their tokens, -1 padded
+ *   bonus [b]           next token at the chosen node: argmax (GREEDY) or a
+ *                       float64 sample from softmax(x / temperature) with
+ *                       counter draw 1 (TYPICAL; same rule as medusa_topk)
+ * ------------------------------------------------------------------------- */
+size_t medusa_accept_workspace(int32_t b, int32_t T);
+int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t* parent,
+                  const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K, int32_t mode,
+                  float temperature, float eps, float delta, uint64_t seed, uint64_t step,
+                  int32_t* L, int32_t* path, int32_t* acc_tokens, int32_t* bonus, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_kv_compact - rollback of the speculative KV entries.
+ * [glossary]: roll back to the last accepted position; the speculative KV
+ * cache manages the tree's key/value entries.  For every sequence s with
+ * P = seq_len[s] (device) and d = 0..L[s]:
+ *   Kc[s, :, P + d, :] <- Kc[s, :, P + path[s, d], :]   (same for Vc)
+ * as if from a snapshot (sources are read before they are overwritten), then
+ * seq_len[s] = P + L[s] + 1.  In place; stale slots past the new length are
+ * left as they are.  Requires path[s, d] >= d (breadth-first node order, as
+ * produced by medusa_accept) and (d * sizeof(dtype)) % 16 == 0.
+ * ------------------------------------------------------------------------- */
+int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
+                      const int32_t* L, int32_t b, int32_t nkv, int32_t Pmax, int32_t d, int32_t K,
+                      int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_H */

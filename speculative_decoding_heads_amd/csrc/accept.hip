@@ -1,0 +1,247 @@
+// Greedy / typical acceptance, path choice and the next token.
+//
+// aiunderstanding.org "Medusa Decoding Heads" ("Deep Dive"): accept the longest
+// prefix that matches what the model would have produced; inferensys.com
+// "Medusa Heads": stop at the first rejection, roll back to the last accepted
+// position, the base model supplies the next token; aicassindra.com "Medusa
+// deep dive" ("Typical acceptance, not exact rejection sampling"): accept a
+// token whose probability exceeds min(eps, delta * exp(-H)), H the entropy of
+// the model's distribution.
+//
+// Conventions: greedy argmax ties go to the lower vocabulary index; typical
+// uses q = softmax(x / T), natural-log entropy and a strict '>'.  A node is
+// fully accepted when it and every ancestor below the root is accepted;
+// L = the largest depth of a fully accepted node, the chosen node the lowest
+// node index at that depth.  Next token: argmax there (greedy) or a seeded
+// float64 sample from softmax(x / T) there (typical, counter draw 1).
+//
+// Kernels:
+//   accept_stats: one workgroup per (sequence, node) row of base logits; a
+//     single streaming pass with 16-byte loads.  Greedy: argmax key.  Typical:
+//     online (m, s, t) with s = sum e^(x'-m), t = sum e^(x'-m)(x'-m),
+//     x' = x / T, rescaled whenever the running max moves; then
+//     H = ln s - t/s and log q(tok) = x'_tok - m - ln s.
+//   accept_walk: one workgroup per sequence: local flags, full-path flags by
+//     walking ancestors, block max/min for L and the chosen node, path and
+//     accepted tokens.
+//   typical mode then runs the shared float64 row sampler on the chosen node.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+
+struct Stat {
+  float m, s, t, pad;
+};
+
+__device__ __forceinline__ void stat_add(float& m, float& s, float& t, float x) {
+  if (x <= m) {
+    const float d = x - m;
+    const float e = expf(d);
+    s += e;
+    t = fmaf(e, d, t);
+  } else {
+    if (s > 0.f) {
+      const float d = m - x;          // < 0
+      const float r = expf(d);
+      t = r * fmaf(d, s, t);
+      s = fmaf(r, s, 1.f);
+    } else {
+      s = 1.f;
+      t = 0.f;
+    }
+    m = x;
+  }
+}
+
+__device__ __forceinline__ void stat_merge(float& m, float& s, float& t, float m2, float s2,
+                                           float t2) {
+  if (s2 == 0.f) return;
+  if (s == 0.f) {
+    m = m2; s = s2; t = t2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  const float d1 = m - M, d2 = m2 - M;
+  const float r1 = expf(d1), r2 = expf(d2);
+  t = r1 * fmaf(d1, s, t) + r2 * fmaf(d2, s2, t2);
+  s = r1 * s + r2 * s2;
+  m = M;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void accept_stats(const float* __restrict__ logits, int V,
+                                                    float inv_temp, int* __restrict__ amax,
+                                                    Stat* __restrict__ stats) {
+  const int64_t row = blockIdx.x;
+  const float* x = logits + row * V;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (MODE == kGreedy) {
+    uint64_t best = 0;
+    if ((V & 3) == 0) {
+      for (int e = 4 * tid; e < V; e += 1024) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t k = make_key(v[i], e + i);
+          best = k > best ? k : best;
+        }
+      }
+    } else {
+      for (int e = tid; e < V; e += 256) {
+        const uint64_t k = make_key(x[e], e);
+        best = k > best ? k : best;
+      }
+    }
+    best = wave_max_u64(best);
+    __shared__ uint64_t sb[4];
+    if (lane == 0) sb[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t b = sb[0];
+      for (int w = 1; w < 4; ++w) b = sb[w] > b ? sb[w] : b;
+      amax[row] = (int)key_index(b);
+    }
+  } else {
+    float m = -INFINITY, s = 0.f, t = 0.f;
+    if ((V & 3) == 0) {
+      for (int e = 4 * tid; e < V; e += 1024) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stat_add(m, s, t, v[i] * inv_temp);
+      }
+    } else {
+      for (int e = tid; e < V; e += 256) stat_add(m, s, t, x[e] * inv_temp);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), t2 = __shfl_xor(t, o, 64);
+      stat_merge(m, s, t, m2, s2, t2);
+    }
+    __shared__ float sm[4][3];
+    if (lane == 0) { sm[wave][0] = m; sm[wave][1] = s; sm[wave][2] = t; }
+    __syncthreads();
+    if (tid == 0) {
+      float M = sm[0][0], S = sm[0][1], Tt = sm[0][2];
+      for (int w = 1; w < 4; ++w) stat_merge(M, S, Tt, sm[w][0], sm[w][1], sm[w][2]);
+      stats[row] = Stat{M, S, Tt, 0.f};
+    }
+  }
+}
+
+__device__ __forceinline__ bool full_path(int c, const int* sparent, const unsigned char* local) {
+  bool full = true;
+  for (int a = c; a > 0;) {
+    full = full && local[a];
+    const int p = sparent[a];
+    if (p < 0 || p >= a) return false;
+    a = p;
+  }
+  return full;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ logits,
+                                                   const int* __restrict__ tokens,
+                                                   const int* __restrict__ parent,
+                                                   const int* __restrict__ depth, int T, int V,
+                                                   int K, float inv_temp, float eps, float delta,
+                                                   const int* __restrict__ amax,
+                                                   const Stat* __restrict__ stats,
+                                                   int* __restrict__ Lout, int* __restrict__ path,
+                                                   int* __restrict__ acc_tokens,
+                                                   int* __restrict__ bonus, int* __restrict__ best_out) {
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ unsigned char local[kMaxT];
+  __shared__ int sdepth[kMaxT], sparent[kMaxT];
+  __shared__ int bestL, bestNode;
+  if (tid == 0) { bestL = 0; bestNode = 0x7fffffff; }
+  for (int c = tid; c < T; c += blockDim.x) {
+    sparent[c] = parent[c];
+    sdepth[c] = depth[c];
+    bool ok = (c == 0);
+    if (c > 0) {
+      const int p = parent[c];
+      const int tok = tokens[(int64_t)s * T + c];
+      const int64_t prow = (int64_t)s * T + p;
+      if (tok >= 0 && tok < V && p >= 0 && p < c) {
+        if (MODE == kGreedy) {
+          ok = tok == amax[prow];
+        } else {
+          const Stat st = stats[prow];
+          const double lns = log((double)st.s);
+          const double H = lns - (double)st.t / (double)st.s;
+          const double logq = (double)(logits[prow * V + tok] * inv_temp) - (double)st.m - lns;
+          const double thr = fmin((double)eps, (double)delta * exp(-H));
+          ok = exp(logq) > thr;
+        }
+      }
+    }
+    local[c] = ok;
+  }
+  __syncthreads();
+  // A parent table is valid when 0 <= parent[c] < c; anything else is treated
+  // as a rejected node, so the walks below always end.
+  for (int c = tid; c < T; c += blockDim.x) {
+    if (full_path(c, sparent, local)) atomicMax(&bestL, sdepth[c]);
+  }
+  __syncthreads();
+  for (int c = tid; c < T; c += blockDim.x) {
+    if (full_path(c, sparent, local) && sdepth[c] == bestL) atomicMin(&bestNode, c);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int L = bestL, best = bestNode;
+    Lout[s] = L;
+    for (int d = L + 1; d <= K; ++d) {
+      path[(int64_t)s * (K + 1) + d] = -1;
+      acc_tokens[(int64_t)s * (K + 1) + d] = -1;
+    }
+    int a = best;
+    for (int d = L; d >= 0; --d) {
+      path[(int64_t)s * (K + 1) + d] = a;
+      acc_tokens[(int64_t)s * (K + 1) + d] = tokens[(int64_t)s * T + a];
+      a = a > 0 ? sparent[a] : 0;
+    }
+    if (MODE == kGreedy) bonus[s] = amax[(int64_t)s * T + best];
+    best_out[s] = best;
+  }
+}
+
+size_t accept_workspace(int b, int T) {
+  // amax / stats per node row, plus the chosen node per sequence
+  size_t rows = (size_t)b * T;
+  return rows * sizeof(Stat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 64;
+}
+
+hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
+                      const int* depth, int b, int T, int V, int K, int mode, float temperature,
+                      float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
+                      int* acc_tokens, int* bonus, void* ws, hipStream_t st) {
+  const size_t rows = (size_t)b * T;
+  Stat* stats = static_cast<Stat*>(ws);
+  int* amax = reinterpret_cast<int*>(stats + rows);
+  int* best = amax + rows;
+  const float inv_temp = 1.0f / temperature;
+  if (mode == kGreedy) {
+    hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(256), 0, st, base_logits,
+                       V, inv_temp, amax, stats);
+    hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
+                       parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
+                       acc_tokens, bonus, best);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(256), 0, st, base_logits,
+                     V, inv_temp, amax, stats);
+  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
+                     depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,
+                     best);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,
+                         st);
+}
+
+}  // namespace medusa

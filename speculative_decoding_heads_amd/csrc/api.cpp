@@ -1,0 +1,302 @@
+// C ABI of libmedusa.so (declared in include/medusa.h): argument validation,
+// workspace sizing and dispatch to the HIP kernels.  Host code only.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/medusa.h"
+#include "kernels.h"
+#include "tree_plan.h"
+
+using namespace medusa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const std::string& msg) {
+  g_err = msg;
+  return status;
+}
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MEDUSA_OK;
+  return fail(MEDUSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int32_t dt) { return dt == MEDUSA_F32 || dt == MEDUSA_BF16; }
+size_t elem_size(int32_t dt) { return dt == MEDUSA_BF16 ? 2 : 4; }
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_k(const int32_t* k_host, int32_t K, int32_t kmax_or_zero) {
+  if (!k_host) return fail(MEDUSA_ERR_ARG, "k_host is NULL");
+  if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
+  for (int i = 0; i < K; ++i) {
+    if (k_host[i] < 1 || k_host[i] > MEDUSA_MAX_K)
+      return fail(MEDUSA_ERR_ARG, "k_host[i] out of range [1, 16]");
+    if (kmax_or_zero > 0 && k_host[i] > kmax_or_zero)
+      return fail(MEDUSA_ERR_ARG, "k_host[i] exceeds kmax");
+  }
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_abi_version(void) { return MEDUSA_ABI_VERSION; }
+
+const char* medusa_status_str(int status) {
+  switch (status) {
+    case MEDUSA_OK: return "ok";
+    case MEDUSA_ERR_ARG: return "invalid argument";
+    case MEDUSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MEDUSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MEDUSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* medusa_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------- heads
+size_t medusa_heads_workspace(int64_t rows, int32_t H, int32_t n_heads, int32_t include_base,
+                              int32_t dtype) {
+  if (rows <= 0 || H <= 0 || n_heads <= 0 || !dtype_ok(dtype)) return 0;
+  const int R = include_base + n_heads;
+  return round_up((size_t)rows * R * H * elem_size(dtype));
+}
+
+int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t n_heads,
+                 const void* LM, int32_t V, int32_t dtype, int32_t include_base, void* u_out,
+                 float* logits, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0) return fail(MEDUSA_ERR_ARG, "rows < 0");
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (H <= 0 || V <= 0) return fail(MEDUSA_ERR_ARG, "H and V must be positive");
+  if (n_heads < 0 || n_heads > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "n_heads out of range");
+  if (include_base != 0 && include_base != 1) return fail(MEDUSA_ERR_ARG, "include_base must be 0 or 1");
+  const int R = include_base + n_heads;
+  if (R < 1) return fail(MEDUSA_ERR_ARG, "no output head requested");
+  if (rows == 0) return MEDUSA_OK;
+  if (!x || !LM || !logits) return fail(MEDUSA_ERR_ARG, "x, LM and logits must be non-NULL");
+  if (n_heads > 0 && !W) return fail(MEDUSA_ERR_ARG, "W is NULL with n_heads > 0");
+  if (rows * R > INT32_MAX / 2 || (int64_t)n_heads * H > INT32_MAX / 2)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "too many rows");
+  if (dtype == MEDUSA_BF16) {
+    if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "bf16 heads need H % 128 == 0");
+    if (!aligned16(x) || !aligned16(LM) || (W && !aligned16(W)) || (u_out && !aligned16(u_out)))
+      return fail(MEDUSA_ERR_ARG, "bf16 operands must be 16-byte aligned");
+  }
+  hipStream_t st = as_stream(stream);
+  const void* gemm_x = x;
+  if (n_heads > 0 || u_out) {
+    void* u = u_out;
+    if (!u) {
+      const size_t need = medusa_heads_workspace(rows, H, n_heads, include_base, dtype);
+      if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "heads: workspace too small");
+      u = ws;
+    }
+    int s = hip_status(run_heads_hidden(x, (int)rows, H, W, n_heads, dtype, u, R, include_base, st),
+                       "heads hidden");
+    if (s) return s;
+    gemm_x = u;
+  }
+  return hip_status(run_lm_logits(gemm_x, (int)(rows * R), H, LM, V, dtype, logits, st),
+                    "LM projection");
+}
+
+// ------------------------------------------------------------------- top-k
+size_t medusa_topk_workspace(int32_t b, int32_t K, int32_t V, int32_t kmax) {
+  if (b <= 0 || K <= 0 || V <= 0 || kmax <= 0) return 0;
+  return round_up(topk_workspace(b, K, V, kmax));
+}
+
+int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
+                int32_t kmax, int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
+                int32_t* root, int32_t* idx, float* val, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
+  if (V <= 0) return fail(MEDUSA_ERR_ARG, "V must be positive");
+  if (kmax < 1 || kmax > MEDUSA_MAX_K) return fail(MEDUSA_ERR_ARG, "kmax out of range [1, 16]");
+  if (int s = check_k(k_host, K, kmax)) return s;
+  for (int i = 0; i < K; ++i)
+    if (k_host[i] > V) return fail(MEDUSA_ERR_ARG, "k_i exceeds V");
+  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL)
+    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY or TYPICAL");
+  if (root_mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  if (b == 0) return MEDUSA_OK;
+  if (!logits || !root || !idx || !val) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if ((int64_t)b * (K + 1) > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (K+1) > 65535");
+  const size_t need = medusa_topk_workspace(b, K, V, kmax);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
+  TopkArgs a{};
+  a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
+  a.temperature = temperature; a.seed = seed; a.step = step;
+  for (int i = 0; i < K; ++i) a.k[i] = k_host[i];
+  return hip_status(run_topk(logits, a, root, idx, val, ws, as_stream(stream)), "topk");
+}
+
+// ------------------------------------------------------------------- tree
+static int plan_for(const int32_t* k_host, int32_t K, int32_t N, int32_t dn, int32_t dd,
+                    std::shared_ptr<const TreePlanHost>* out) {
+  if (int s = check_k(k_host, K, 0)) return s;
+  if (N < -1) return fail(MEDUSA_ERR_ARG, "N must be >= 0, or -1 for the full tree");
+  if (dn <= 0 || dd <= 0 || dn >= dd || dd > 1000000)
+    return fail(MEDUSA_ERR_ARG, "decay must be a fraction in (0, 1)");
+  const int64_t total = full_tree_candidates(k_host, K);
+  if (N > total && total >= 0) return fail(MEDUSA_ERR_ARG, "N exceeds the candidate count");
+  const int64_t keep = N < 0 ? total : N;
+  if (keep < 0 || keep + 1 > MEDUSA_MAX_T) return fail(MEDUSA_ERR_UNSUPPORTED, "tree exceeds 256 nodes");
+  std::string err;
+  auto p = get_tree_plan(k_host, K, N, dn, dd, &err);
+  if (!p) return fail(MEDUSA_ERR_UNSUPPORTED, err);
+  *out = p;
+  return MEDUSA_OK;
+}
+
+int medusa_tree_plan(const int32_t* k_host, int32_t K, int32_t N, int32_t decay_num,
+                     int32_t decay_den, int32_t* parent, int32_t* depth, int32_t* rank,
+                     int32_t T_cap, int32_t* T_out) {
+  std::shared_ptr<const TreePlanHost> p;
+  if (int s = plan_for(k_host, K, N, decay_num, decay_den, &p)) return s;
+  if (T_out) *T_out = p->T;
+  if (!parent && !depth && !rank) return MEDUSA_OK;
+  if (T_cap < p->T) return fail(MEDUSA_ERR_ARG, "T_cap smaller than the tree");
+  for (int i = 0; i < p->T; ++i) {
+    if (parent) parent[i] = p->parent[i];
+    if (depth) depth[i] = p->depth[i];
+    if (rank) rank[i] = p->rank[i];
+  }
+  return MEDUSA_OK;
+}
+
+int medusa_build_tree(const int32_t* k_host, int32_t K, int32_t N, int32_t decay_num,
+                      int32_t decay_den, const int32_t* root, const int32_t* idx, int32_t b,
+                      int32_t kmax, const int32_t* seq_len, int32_t* tokens, int32_t* pos,
+                      int32_t* parent, int32_t* depth, uint64_t* anc, int32_t anc_words,
+                      void* stream) {
+  std::shared_ptr<const TreePlanHost> p;
+  if (int s = plan_for(k_host, K, N, decay_num, decay_den, &p)) return s;
+  if (kmax < 1 || kmax > MEDUSA_MAX_K) return fail(MEDUSA_ERR_ARG, "kmax out of range [1, 16]");
+  for (int i = 0; i < K; ++i)
+    if (k_host[i] > kmax) return fail(MEDUSA_ERR_ARG, "k_i exceeds kmax");
+  if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
+  if (anc_words < (p->T + 63) / 64) return fail(MEDUSA_ERR_ARG, "anc_words < ceil(T / 64)");
+  if (b == 0) return MEDUSA_OK;
+  if (!root || !idx || !seq_len || !tokens || !pos || !parent || !depth || !anc)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  TreeDev t{};
+  t.T = p->T; t.K = K; t.kmax = kmax; t.anc_words = anc_words;
+  for (int i = 0; i < p->T; ++i) {
+    t.parent[i] = (int16_t)p->parent[i];
+    t.depth[i] = (uint8_t)p->depth[i];
+    t.rank[i] = (uint8_t)(p->rank[i] < 0 ? 0 : p->rank[i]);
+  }
+  return hip_status(run_build_tree(t, root, idx, b, seq_len, tokens, pos, parent, depth, anc,
+                                   as_stream(stream)),
+                    "build_tree");
+}
+
+// ------------------------------------------------------------------- attention
+static int attn_check(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d, int32_t Pmax,
+                      int32_t dtype) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
+  if (nq < 1 || nkv < 1 || nq % nkv != 0) return fail(MEDUSA_ERR_ARG, "need nq % nkv == 0");
+  if (Pmax < T) return fail(MEDUSA_ERR_ARG, "Pmax < T");
+  if (dtype == MEDUSA_BF16 && d != 64 && d != 128)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "bf16 attention supports d = 64 or 128");
+  if (dtype == MEDUSA_F32 && (d < 1 || d > 256))
+    return fail(MEDUSA_ERR_UNSUPPORTED, "f32 attention supports d <= 256");
+  if (dtype == MEDUSA_F32 && Pmax > 16384)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "f32 attention supports Pmax <= 16384");
+  if ((int64_t)b * nkv * ((Pmax + 63) / 64) * ((T * (nq / nkv) + 63) / 64) > INT32_MAX / 4)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "attention grid too large");
+  if (dtype == MEDUSA_F32 && (int64_t)b * T * nq > INT32_MAX / 2)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "attention grid too large");
+  return MEDUSA_OK;
+}
+
+size_t medusa_tree_attn_workspace(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d,
+                                  int32_t Pmax, int32_t dtype) {
+  if (b <= 0 || T < 1 || nq < 1 || nkv < 1 || nq % nkv || Pmax < T || !dtype_ok(dtype)) return 0;
+  return round_up(attn_plan(b, T, nq, nkv, d, Pmax, dtype).ws_bytes);
+}
+
+int medusa_tree_attn(const void* Q, const void* Kc, const void* Vc, const int32_t* seq_len,
+                     const uint64_t* anc, int32_t anc_words, int32_t b, int32_t T, int32_t nq,
+                     int32_t nkv, int32_t d, int32_t Pmax, float scale, int32_t dtype, void* O,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (int s = attn_check(b, T, nq, nkv, d, Pmax, dtype)) return s;
+  if (anc_words < (T + 63) / 64 || anc_words > MEDUSA_MAX_T / 64)
+    return fail(MEDUSA_ERR_ARG, "anc_words must be in [ceil(T/64), 4]");
+  if (!std::isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale must be finite");
+  if (b == 0) return MEDUSA_OK;
+  if (!Q || !Kc || !Vc || !seq_len || !anc || !O) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (dtype == MEDUSA_BF16 && (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O)))
+    return fail(MEDUSA_ERR_ARG, "bf16 attention operands must be 16-byte aligned");
+  AttnPlan p = attn_plan(b, T, nq, nkv, d, Pmax, dtype);
+  if (p.ws_bytes && (!ws || ws_bytes < p.ws_bytes))
+    return fail(MEDUSA_ERR_WORKSPACE, "tree_attn: workspace too small");
+  return hip_status(run_tree_attn(Q, Kc, Vc, seq_len, anc, anc_words, b, T, nq, nkv, d, Pmax, scale,
+                                  dtype, O, ws, p, as_stream(stream)),
+                    "tree_attn");
+}
+
+// ------------------------------------------------------------------- accept
+size_t medusa_accept_workspace(int32_t b, int32_t T) {
+  if (b <= 0 || T <= 0) return 0;
+  return round_up(accept_workspace(b, T));
+}
+
+int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t* parent,
+                  const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K, int32_t mode,
+                  float temperature, float eps, float delta, uint64_t seed, uint64_t step,
+                  int32_t* L, int32_t* path, int32_t* acc_tokens, int32_t* bonus, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "V must be positive");
+  if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
+  if (mode == MEDUSA_TYPICAL) {
+    if (!(temperature > 0.f && std::isfinite(temperature)))
+      return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+    if (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta)))
+      return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
+  }
+  if (b == 0) return MEDUSA_OK;
+  if (!base_logits || !tokens || !parent || !depth || !L || !path || !acc_tokens || !bonus)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if ((int64_t)b * T > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "b * T too large");
+  const size_t need = medusa_accept_workspace(b, T);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
+  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
+  return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,
+                               delta, seed, step, L, path, acc_tokens, bonus, ws,
+                               as_stream(stream)),
+                    "accept");
+}
+
+// ------------------------------------------------------------------- compaction
+int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
+                      const int32_t* L, int32_t b, int32_t nkv, int32_t Pmax, int32_t d, int32_t K,
+                      int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (b < 0 || nkv < 1 || Pmax < 1 || d < 1) return fail(MEDUSA_ERR_ARG, "bad shape");
+  if (K < 0 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [0, 16]");
+  if ((d * elem_size(dtype)) % 16 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d * sizeof(dtype) must be a multiple of 16");
+  if (b == 0) return MEDUSA_OK;
+  if (!Kc || !Vc || !seq_len || !path || !L) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(Kc) || !aligned16(Vc)) return fail(MEDUSA_ERR_ARG, "cache must be 16-byte aligned");
+  return hip_status(run_kv_compact(Kc, Vc, seq_len, path, L, b, nkv, Pmax, d, K, dtype,
+                                   as_stream(stream)),
+                    "kv_compact");
+}
+
+}  // extern "C"

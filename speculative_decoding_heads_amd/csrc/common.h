@@ -1,0 +1,110 @@
+// Device helpers shared by the Medusa HIP kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace medusa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> f32 -----------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- MFMA ---------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16.  Lane l supplies A[l%16][slot 8*(l/16)+j] and
+// B[slot 8*(l/16)+j][l%16], j = 0..7, and receives D[4*(l/16)+i][l%16],
+// i = 0..3.  Kernels pair A and B slots themselves, so any fixed assignment
+// of contraction indices to slots is valid as long as both operands use it.
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- loads ----------------------------------------------------------------------
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming (single-use) load: non-temporal hint so it does not evict reused lines.
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 r;
+  r.x = __builtin_nontemporal_load(&q->x);
+  r.y = __builtin_nontemporal_load(&q->y);
+  r.z = __builtin_nontemporal_load(&q->z);
+  r.w = __builtin_nontemporal_load(&q->w);
+  return r;
+}
+
+// ---- wave reductions ------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---- order-preserving key for (value desc, index asc) selection ---------------
+// key = ord(x) << 32 | (0xffffffff - idx); a larger key is a larger value, and
+// among equal values the lower index.  -0.0 is folded onto +0.0.  Key 0 is
+// below every real key and marks an empty slot.
+__device__ __forceinline__ uint32_t float_ord(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float ord_float(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ uint64_t make_key(float x, uint32_t idx) {
+  return ((uint64_t)float_ord(x) << 32) | (uint64_t)(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+__device__ __forceinline__ float key_value(uint64_t k) { return ord_float((uint32_t)(k >> 32)); }
+
+// ---- counter-based uniform draws (SplitMix64, Steele/Lea/Flood 2014) ---------
+__device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+// u in [0,1) with 24 random bits from (seed, step, seq, draw).
+__device__ __forceinline__ double counter_uniform(uint64_t seed, uint64_t step, uint64_t seq,
+                                                  uint64_t draw) {
+  uint64_t x = splitmix64(seed ^ (step << 32) ^ (seq << 8) ^ draw);
+  return (double)(x >> 40) * (1.0 / 16777216.0);
+}
+
+}  // namespace medusa

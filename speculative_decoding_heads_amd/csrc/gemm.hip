@@ -1,0 +1,394 @@
+// Medusa heads and LM projection: C[m, n] = sum_k X[m, k] * W[n, k].
+//
+// Head formula (aicassindra.com "Medusa deep dive", "The heads are residual
+// blocks, not linear layers"): head_i(h) = LMproj(h + SiLU(W_i h)); the heads
+// run off one hidden state as a few small matmuls.  Both products here are
+// "NT" GEMMs: activations X [M, K] and weights W [N, K] are row-major with the
+// contraction dimension contiguous.
+//
+//   * W_i stage: X = h [b, H], W = all heads stacked [K*H, H]; epilogue
+//     u = h + SiLU(z) stored in bf16 (or f32).
+//   * LM stage: X = u [b*(K+1), H] (or the attention output on the verify
+//     pass), W = LMproj [V, H]; fp32 logits.
+//
+// bf16 kernels use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  W rows
+// are the MFMA "A" rows, X rows the "B" columns, so each lane ends up with 4
+// consecutive n of one output row (one 16-byte store of logits).
+//
+// Two bf16 kernels:
+//   gemm_skinny : M <= 80.  HBM-bound weight stream.  A workgroup owns 16*NB
+//                 weight rows; its 4 waves split K and reduce through LDS.
+//                 Both operands go global -> registers (X is tiny and stays in
+//                 L2); each lane loads 64 contiguous bytes per row per step.
+//   gemm_tiled  : larger M.  A workgroup owns BM = 16*MB activation rows
+//                 (staged in LDS, shared by its 4 waves) and 64*NBW weight rows
+//                 (16*NBW per wave, direct loads).  Tiles are mapped to XCDs so
+//                 that the M-tiles of one weight tile run on one XCD (L2 reuse).
+// One f32 kernel (tiny fp32 workload): one wave per weight row.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+
+// ---------------------------------------------------------------- epilogues
+struct EpiLogits {
+  float* C;
+  int64_t ldc;
+  int M, N;
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M || n >= N) return;
+    float* p = C + (int64_t)m * ldc + n;
+    if (n + 3 < N && ((((uintptr_t)p) & 15) == 0)) {
+      *reinterpret_cast<f32x4*>(p) = v;
+    } else {
+      for (int i = 0; i < 4 && n + i < N; ++i) p[i] = v[i];
+    }
+  }
+  __device__ __forceinline__ void store1(int m, int n, float v) const {
+    if (m < M && n < N) C[(int64_t)m * ldc + n] = v;
+  }
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// u[m, base + i, o] = x[m, o] + SiLU(z[m, i*H + o])   (n = i*H + o)
+template <typename T>
+struct EpiHeads {
+  T* U;                 // [M, R, H]
+  const T* X;           // [M, ldx]
+  int64_t ldx;
+  int H, R, base, M, N;
+  __device__ __forceinline__ void store1(int m, int n, float z) const {
+    if (m >= M || n >= N) return;
+    int i = n / H, o = n - i * H;
+    float x;
+    if constexpr (sizeof(T) == 2) x = bf16_to_f32(X[(int64_t)m * ldx + o]);
+    else x = X[(int64_t)m * ldx + o];
+    float u = x + silu_f(z);
+    T* p = U + ((int64_t)m * R + base + i) * H + o;
+    if constexpr (sizeof(T) == 2) *p = f32_to_bf16(u);
+    else *p = u;
+  }
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M || n >= N) return;
+    if constexpr (sizeof(T) == 2) {
+      if (n + 3 < N && (H & 3) == 0) {       // 4 consecutive o inside one head
+        int i = n / H, o = n - i * H;
+        uint2 xw = *reinterpret_cast<const uint2*>(X + (int64_t)m * ldx + o);
+        float u0 = bf16_lo(xw.x) + silu_f(v[0]);
+        float u1 = bf16_hi(xw.x) + silu_f(v[1]);
+        float u2 = bf16_lo(xw.y) + silu_f(v[2]);
+        float u3 = bf16_hi(xw.y) + silu_f(v[3]);
+        uint2 out;
+        out.x = pack_bf16x2(u0, u1);
+        out.y = pack_bf16x2(u2, u3);
+        *reinterpret_cast<uint2*>(U + ((int64_t)m * R + base + i) * H + o) = out;
+        return;
+      }
+    }
+    for (int j = 0; j < 4; ++j) store1(m, n + j, v[j]);
+  }
+};
+
+// ---------------------------------------------------------------- skinny bf16
+// grid.x = ceil(N / (16*NB)); block = 256 (4 waves splitting K in 128-chunks).
+template <int NB, int MB, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restrict__ X,
+                                                        int64_t ldx, int M,
+                                                        const uint16_t* __restrict__ W,
+                                                        int N, int Kd, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NB;
+  const int nchunks = Kd >> 7;
+  const int c_begin = (nchunks * wave) >> 2, c_end = (nchunks * (wave + 1)) >> 2;
+
+  const uint16_t* wp[NB];
+  const uint16_t* xp[MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int n = min(n0 + 16 * nb + r16, N - 1);
+    wp[nb] = W + (int64_t)n * Kd + 32 * g4;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    int m = min(16 * mb + r16, M - 1);
+    xp[mb] = X + (int64_t)m * ldx + 32 * g4;
+  }
+
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wa[NB][4], xb[MB][4];
+  if (c_begin < c_end) {
+    const int k0 = c_begin << 7;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[nb][s] = ldg16_stream(wp[nb] + k0 + 8 * s);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xb[mb][s] = ldg16(xp[mb] + k0 + 8 * s);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int kn = (c + 1 < c_end ? c + 1 : c) << 7;
+    uint4 wn[NB][4], xn[MB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wn[nb][s] = ldg16_stream(wp[nb] + kn + 8 * s);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xn[mb][s] = ldg16(xp[mb] + kn + 8 * s);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16x16x32(wa[nb][s], xb[mb][s], acc[nb][mb]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[nb][s] = wn[nb][s];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xb[mb][s] = xn[mb][s];
+  }
+
+  // cross-wave reduction of the 4 K-partials
+  __shared__ f32x4 red[4][NB * MB][64];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[wave][nb * MB + mb][lane] = acc[nb][mb];
+  __syncthreads();
+  for (int p = wave; p < NB * MB; p += 4) {
+    f32x4 v = red[0][p][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      f32x4 t = red[w][p][lane];
+      v[0] += t[0]; v[1] += t[1]; v[2] += t[2]; v[3] += t[3];
+    }
+    const int nb = p / MB, mb = p - nb * MB;
+    epi.store4(16 * mb + r16, n0 + 16 * nb + 4 * g4, v);
+  }
+}
+
+// ---------------------------------------------------------------- tiled bf16
+// Tile index t -> (n tile, m tile) with all m tiles of one n tile adjacent on
+// one XCD (workgroups are dispatched round-robin over the 8 XCDs).
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int x = b & 7, j = b >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + min(x, r) + j;
+}
+
+template <int MB, int NBW, class Epi>
+__global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restrict__ X, int64_t ldx,
+                                                       int M, const uint16_t* __restrict__ W,
+                                                       int N, int Kd, int ntm, Epi epi) {
+  constexpr int BM = 16 * MB;
+  constexpr int BN = 64 * NBW;
+  constexpr int LDSROW = 128 + 8;              // bf16 elements per LDS row (16 B pad)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDSROW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int total = gridDim.x;
+  const int t = xcd_tile(blockIdx.x, total);
+  const int tm = t % ntm, tn = t / ntm;
+  const int m0 = tm * BM, n0 = tn * BN + wave * 16 * NBW;
+  const int nchunks = Kd >> 7;
+
+  const uint16_t* wp[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    int n = min(n0 + 16 * nb + r16, N - 1);
+    wp[nb] = W + (int64_t)n * Kd + 32 * g4;
+  }
+  // X tile loader: BM rows x 256 B per chunk = 16*BM pieces of 16 B
+  constexpr int XPIECES = BM * 16 / 256;       // per thread (= MB)
+  const uint16_t* xsrc[XPIECES];
+  int xdst[XPIECES];
+#pragma unroll
+  for (int i = 0; i < XPIECES; ++i) {
+    int piece = threadIdx.x + 256 * i;
+    int row = piece >> 4, part = piece & 15;
+    int m = min(m0 + row, M - 1);
+    xsrc[i] = X + (int64_t)m * ldx + part * 8;
+    xdst[i] = row * LDSROW + part * 8;
+  }
+
+  f32x4 acc[NBW][MB];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wa[NBW][4], xr[XPIECES];
+#pragma unroll
+  for (int i = 0; i < XPIECES; ++i) xr[i] = ldg16(xsrc[i]);
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wa[nb][s] = ldg16(wp[nb] + 8 * s);
+#pragma unroll
+  for (int i = 0; i < XPIECES; ++i) *reinterpret_cast<uint4*>(&xs[0][xdst[i]]) = xr[i];
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const int kn = (c + 1 < nchunks ? c + 1 : c) << 7;
+    uint4 wn[NBW][4];
+#pragma unroll
+    for (int i = 0; i < XPIECES; ++i) xr[i] = ldg16(xsrc[i] + kn);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wn[nb][s] = ldg16(wp[nb] + kn + 8 * s);
+    const uint16_t* xb = &xs[buf][r16 * LDSROW + 32 * g4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * s);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[nb][mb] = mfma16x16x32(wa[nb][s], b, acc[nb][mb]);
+      }
+    }
+    if (c + 1 < nchunks) {
+#pragma unroll
+      for (int i = 0; i < XPIECES; ++i) *reinterpret_cast<uint4*>(&xs[buf ^ 1][xdst[i]]) = xr[i];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[nb][s] = wn[nb][s];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 16 * nb + 4 * g4, acc[nb][mb]);
+}
+
+// ---------------------------------------------------------------- f32
+// One wave per weight row n; lanes split K; M <= 64 rows, looped in groups of 8.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_rowwave_f32(const float* __restrict__ X, int64_t ldx,
+                                                        int M, const float* __restrict__ W, int N,
+                                                        int Kd, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 4 + wave;
+  if (n >= N) return;
+  const float* w = W + (int64_t)n * Kd;
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int k = lane; k < Kd; k += 64) {
+      float wv = w[k];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (m0 + j < M) acc[j] = fmaf(wv, X[(int64_t)(m0 + j) * ldx + k], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float s = wave_sum(acc[j]);
+      if (lane == 0 && m0 + j < M) epi.store1(m0 + j, n, s);
+    }
+  }
+}
+
+// copy x rows into slot 0 of u (the base head's hidden state is h itself)
+template <typename T>
+__global__ void copy_base_rows(T* U, const T* X, int64_t ldx, int M, int H, int R) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)M * H;
+  if (i >= total) return;
+  int m = (int)(i / H), o = (int)(i - (int64_t)m * H);
+  U[(int64_t)m * R * H + o] = X[(int64_t)m * ldx + o];
+}
+
+// ---------------------------------------------------------------- launchers
+template <class Epi>
+static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
+                              int Kd, const Epi& epi, hipStream_t st) {
+  const int mb = (M + 15) / 16;
+  if (M <= 80) {
+    // skinny: NB chosen so that the LDS reduction stays <= 64 KB
+#define SKINNY(NB_, MB_)                                                                     \
+  hipLaunchKernelGGL((gemm_skinny_bf16<NB_, MB_, Epi>), dim3((N + 16 * NB_ - 1) / (16 * NB_)), \
+                     dim3(256), 0, st, X, ldx, M, W, N, Kd, epi)
+    switch (mb) {
+      case 1: SKINNY(2, 1); break;
+      case 2: SKINNY(2, 2); break;
+      case 3: SKINNY(2, 3); break;
+      case 4: SKINNY(2, 4); break;
+      default: SKINNY(2, 5); break;
+    }
+#undef SKINNY
+  } else {
+    constexpr int MB = 8, NBW = 4;
+    const int ntm = (M + 16 * MB - 1) / (16 * MB);
+    const int ntn = (N + 64 * NBW - 1) / (64 * NBW);
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB, NBW, Epi>), dim3(ntm * ntn), dim3(256), 0, st, X, ldx,
+                       M, W, N, Kd, ntm, epi);
+  }
+  return hipGetLastError();
+}
+
+template <class Epi>
+static hipError_t launch_f32(const float* X, int64_t ldx, int M, const float* W, int N, int Kd,
+                             const Epi& epi, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_rowwave_f32<Epi>), dim3((N + 3) / 4), dim3(256), 0, st, X, ldx, M, W,
+                     N, Kd, epi);
+  return hipGetLastError();
+}
+
+hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_heads, int dtype,
+                            void* u, int R, int base, hipStream_t st) {
+  const int N = n_heads * H;
+  if (dtype == kBF16) {
+    const uint16_t* X = static_cast<const uint16_t*>(x);
+    uint16_t* U = static_cast<uint16_t*>(u);
+    if (base) {
+      int64_t tot = (int64_t)M * H;
+      hipLaunchKernelGGL(copy_base_rows<uint16_t>, dim3((unsigned)((tot + 255) / 256)), dim3(256),
+                         0, st, U, X, (int64_t)H, M, H, R);
+    }
+    if (n_heads == 0) return hipGetLastError();
+    EpiHeads<uint16_t> epi{U, X, (int64_t)H, H, R, base, M, N};
+    return launch_bf16(X, H, M, static_cast<const uint16_t*>(W), N, H, epi, st);
+  } else {
+    const float* X = static_cast<const float*>(x);
+    float* U = static_cast<float*>(u);
+    if (base) {
+      int64_t tot = (int64_t)M * H;
+      hipLaunchKernelGGL(copy_base_rows<float>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
+                         st, U, X, (int64_t)H, M, H, R);
+    }
+    if (n_heads == 0) return hipGetLastError();
+    EpiHeads<float> epi{U, X, (int64_t)H, H, R, base, M, N};
+    return launch_f32(X, H, M, static_cast<const float*>(W), N, H, epi, st);
+  }
+}
+
+hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
+                         float* logits, hipStream_t st) {
+  EpiLogits epi{logits, (int64_t)V, M, V};
+  if (dtype == kBF16)
+    return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
+                       H, epi, st);
+  return launch_f32(static_cast<const float*>(x), H, M, static_cast<const float*>(LM), V, H, epi,
+                    st);
+}
+
+}  // namespace medusa

@@ -1,0 +1,77 @@
+// Internal launchers of the Medusa HIP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace medusa {
+
+enum { kF32 = 0, kBF16 = 1 };
+enum { kGreedy = 0, kTypical = 1 };
+
+constexpr int kMaxHeads = 16;   // Medusa heads K
+constexpr int kMaxK = 16;       // shortlist size per head
+constexpr int kMaxT = 256;      // tree nodes including the root
+constexpr int kMaxAncWords = kMaxT / 64;
+
+// ---- heads / LM projection (gemm.hip)
+hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_heads, int dtype,
+                            void* u, int R, int base, hipStream_t st);
+hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
+                         float* logits, hipStream_t st);
+
+// ---- top-k shortlists and root (topk.hip)
+struct TopkArgs {
+  int b, K, V, kmax;
+  int root_mode;
+  float temperature;
+  uint64_t seed, step;
+  int k[kMaxHeads];
+};
+size_t topk_workspace(int b, int K, int V, int kmax);
+hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
+                    void* ws, hipStream_t st);
+
+// ---- sampling rows of softmax(x / T) in float64 (topk.hip)
+// Row of sequence s: base + s*seq_stride + (row_sel ? row_sel[s] : 0) * V.
+hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
+                           float temperature, uint64_t seed, uint64_t step, uint64_t draw,
+                           int* out, hipStream_t st);
+
+// ---- tree gather (tree.hip)
+struct TreeDev {
+  int T, K, kmax, anc_words;
+  int16_t parent[kMaxT];
+  uint8_t depth[kMaxT];
+  uint8_t rank[kMaxT];
+};
+hipError_t run_build_tree(const TreeDev& t, const int* root, const int* idx, int b,
+                          const int* seq_len, int* tokens, int* pos, int* parent, int* depth,
+                          uint64_t* anc, hipStream_t st);
+
+// ---- tree attention (attn.hip)
+struct AttnPlan {
+  int nsplit;        // key-range partitions per (sequence, kv head)
+  int rowgroups;     // workgroups along the query rows of one kv head
+  int rb;            // 16-row blocks per wave
+  size_t ws_bytes;
+};
+AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
+hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const int* seq_len,
+                         const uint64_t* anc, int anc_words, int b, int T, int nq, int nkv, int d,
+                         int Pmax, float scale, int dtype, void* O, void* ws, const AttnPlan& p,
+                         hipStream_t st);
+
+// ---- acceptance (accept.hip)
+size_t accept_workspace(int b, int T);
+hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
+                      const int* depth, int b, int T, int V, int K, int mode, float temperature,
+                      float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
+                      int* acc_tokens, int* bonus, void* ws, hipStream_t st);
+
+// ---- compaction (compact.hip)
+hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,
+                          int nkv, int Pmax, int d, int K, int dtype, hipStream_t st);
+
+}  // namespace medusa

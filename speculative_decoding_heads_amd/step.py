@@ -1,0 +1,79 @@
+"""One Medusa draft-and-verify step as a sequence of libmedusa calls.
+
+This module only allocates device buffers (through torch) and enqueues the
+library calls in loop order (inferensys.com "Medusa Heads": draft, verify,
+accept and roll back); every part of the step runs in the HIP kernels.
+
+    heads      : medusa_heads(h)            -> logits [b, K+1, V]
+    shortlists : medusa_topk(logits)        -> root [b], idx [b, K, kmax]
+    tree       : medusa_build_tree          -> tokens, pos, parent, depth, anc
+    verify     : medusa_tree_attn(Q, Kc, Vc)-> O [b, T, nq*d]
+                 medusa_heads(O, base only) -> base_logits [b, T, V]
+    accept     : medusa_accept              -> L, path, acc_tokens, bonus
+    rollback   : medusa_kv_compact          -> Kc, Vc, seq_len updated
+"""
+
+import torch
+
+from . import medusa as M
+
+
+class VerifyStep:
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = c = cfg
+        self.device = device
+        dt = M.BF16 if c.dtype == "bf16" else M.F32
+        self.dt = dt
+        self.mode = M.TYPICAL if c.mode == "typical" else M.GREEDY
+        self.N = c.N
+        T, K = c.T, c.K
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        act = torch.bfloat16 if dt == M.BF16 else torch.float32
+        self.logits = torch.empty(c.b, K + 1, c.V, **f32)
+        self.u = torch.empty(c.b, K + 1, c.H, dtype=act, device=device)
+        self.root = torch.empty(c.b, **i32)
+        self.idx = torch.empty(c.b, K, c.kmax, **i32)
+        self.val = torch.empty(c.b, K, c.kmax, **f32)
+        self.tokens = torch.empty(c.b, T, **i32)
+        self.pos = torch.empty(c.b, T, **i32)
+        self.parent = torch.empty(T, **i32)
+        self.depth = torch.empty(T, **i32)
+        self.anc_words = (T + 63) // 64
+        self.anc = torch.empty(T, self.anc_words, dtype=torch.int64, device=device)
+        self.O = torch.empty(c.b, T, c.nq * c.d, dtype=act, device=device)
+        self.base_logits = torch.empty(c.b, T, c.V, **f32)
+        self.L = torch.empty(c.b, **i32)
+        self.path = torch.empty(c.b, K + 1, **i32)
+        self.acc_tokens = torch.empty(c.b, K + 1, **i32)
+        self.bonus = torch.empty(c.b, **i32)
+        self.ws_topk = M.workspace(M.medusa_topk_workspace(c.b, K, c.V, c.kmax), device)
+        self.ws_attn = M.workspace(
+            M.medusa_tree_attn_workspace(c.b, T, c.nq, c.nkv, c.d, c.Pmax, dt), device)
+        self.ws_acc = M.workspace(M.medusa_accept_workspace(c.b, T), device)
+
+    def run(self, x, step=0, stream=None):
+        """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len."""
+        c = self.cfg
+        M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
+                       stream=stream)
+        M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step, self.root,
+                      self.idx, self.val, self.ws_topk, stream=stream)
+        M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
+                            self.idx, x["seq_len"], self.tokens, self.pos, self.parent,
+                            self.depth, self.anc, stream=stream)
+        M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], self.anc, self.O,
+                           ws=self.ws_attn, stream=stream)
+        M.medusa_heads(self.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
+                       self.base_logits.view(c.b * c.T, c.V), include_base=1, stream=stream)
+        M.medusa_accept(self.base_logits, self.tokens, self.parent, self.depth, c.K, self.mode,
+                        c.temperature, c.eps, c.delta, c.seed, step, self.L, self.path,
+                        self.acc_tokens, self.bonus, self.ws_acc, stream=stream)
+        M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], self.path, self.L, stream=stream)
+
+
+def device_inputs(cfg, host, device="cuda"):
+    """Copy host inputs (from ``synth.make_inputs``) to the device, plus seq_len = P."""
+    x = {k: v.to(device) for k, v in host.items()}
+    x["seq_len"] = torch.full((cfg.b,), cfg.P, dtype=torch.int32, device=device)
+    return x

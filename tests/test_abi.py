@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU.
+
+* libmedusa.so loads and exports every entry point include/medusa.h declares;
+* the host-only tree planner (medusa_tree_plan) equals the oracle's plan;
+* argument validation fails before any launch, with the documented statuses.
+No call here reaches a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import tree_plan
+from speculative_decoding_heads_amd import medusa as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "medusa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH),
+                                reason="libmedusa.so not built")
+
+ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE = -1, -2, -3
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(medusa_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(M.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    L = M.lib()
+    assert L.medusa_abi_version() == 1
+    assert L.medusa_status_str(0) == b"ok"
+    assert L.medusa_status_str(-3).startswith(b"workspace")
+
+
+@pytest.mark.parametrize("k,N", [((2, 2, 1), None), ((10,) * 4, 64), ((10,) * 5, 128),
+                                 ((3, 2), 5), ((4, 3, 2), 9), ((1, 1, 1), None), ((16,), 16),
+                                 ((5, 5, 5), 0)])
+def test_host_tree_plan_matches_oracle(k, N):
+    parent, depth, rank = M.medusa_tree_plan(k, N)
+    ref = tree_plan(k, N)
+    assert parent == [int(x) for x in ref.parent]
+    assert depth == [int(x) for x in ref.depth]
+    assert rank == [-1] + [t[-1] for t in ref.tuples[1:]]
+
+
+def test_host_tree_plan_other_decay():
+    from fractions import Fraction
+    parent, depth, rank = M.medusa_tree_plan((6, 5, 4), 40, 2, 3)
+    ref = tree_plan((6, 5, 4), 40, Fraction(2, 3))
+    assert parent == [int(x) for x in ref.parent] and depth == [int(x) for x in ref.depth]
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_tree_plan_rejections():
+    L = M.lib()
+    T = ctypes.c_int32(0)
+    k = M._i32_host([10, 10])
+    assert L.medusa_tree_plan(k, 2, 111, 4, 5, None, None, None, 0, ctypes.byref(T)) == ERR_ARG
+    assert L.medusa_tree_plan(k, 2, 10, 5, 4, None, None, None, 0, ctypes.byref(T)) == ERR_ARG
+    assert L.medusa_tree_plan(k, 0, 10, 4, 5, None, None, None, 0, ctypes.byref(T)) == ERR_ARG
+    big = M._i32_host([16] * 3)
+    assert L.medusa_tree_plan(big, 3, -1, 4, 5, None, None, None, 0, ctypes.byref(T)) == ERR_UNSUPPORTED
+    assert b"256" in L.medusa_last_error()
+    bad = M._i32_host([0, 3])
+    assert L.medusa_tree_plan(bad, 2, 1, 4, 5, None, None, None, 0, ctypes.byref(T)) == ERR_ARG
+
+
+def test_validation_before_launch():
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+    # heads: negative rows, bad dtype, unaligned bf16, H not a multiple of 128, small workspace
+    assert L.medusa_heads(fake, -1, 128, None, 0, fake, 10, 1, 1, None, fake, None, 0, None) == ERR_ARG
+    assert L.medusa_heads(fake, 1, 128, None, 0, fake, 10, 7, 1, None, fake, None, 0, None) == ERR_ARG
+    assert L.medusa_heads(ctypes.c_void_p(0x1002), 1, 128, None, 0, fake, 10, 1, 1, None, fake,
+                          None, 0, None) == ERR_ARG
+    assert L.medusa_heads(fake, 1, 100, None, 0, fake, 10, 1, 1, None, fake, None, 0, None) == ERR_UNSUPPORTED
+    assert L.medusa_heads(fake, 1, 128, fake, 2, fake, 10, 1, 1, None, fake, None, 0, None) == ERR_WORKSPACE
+    assert L.medusa_heads(fake, 1, 128, None, 2, fake, 10, 1, 1, None, fake, None, 0, None) == ERR_ARG
+    # rows == 0 is a no-op
+    assert L.medusa_heads(None, 0, 128, None, 0, None, 10, 1, 1, None, None, None, 0, None) == 0
+    # topk: k_i > kmax, k_i > V, bad mode, temperature
+    k = M._i32_host([4, 4])
+    assert L.medusa_topk(fake, 1, 2, 100, k, 2, 0, 1.0, 0, 0, fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_topk(fake, 1, 2, 3, k, 4, 0, 1.0, 0, 0, fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_topk(fake, 1, 2, 100, k, 4, 5, 1.0, 0, 0, fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_topk(fake, 1, 2, 100, k, 4, 1, 0.0, 0, 0, fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_topk(fake, 1, 2, 100, k, 4, 0, 1.0, 0, 0, fake, fake, fake, fake, 0, None) == ERR_WORKSPACE
+    # attention: nq % nkv, Pmax < T, d unsupported, anc words
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 5, 6, 4, 128, 100, 0.1, 1, fake,
+                              None, 0, None) == ERR_ARG
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 5, 4, 4, 128, 4, 0.1, 1, fake,
+                              None, 0, None) == ERR_ARG
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 5, 4, 4, 96, 100, 0.1, 1, fake,
+                              None, 0, None) == ERR_UNSUPPORTED
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 100, 4, 4, 128, 200, 0.1, 1, fake,
+                              None, 0, None) == ERR_ARG
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 300, 4, 4, 128, 400, 0.1, 1, fake,
+                              None, 0, None) == ERR_ARG
+    # accept: bad mode, typical without temperature, small workspace
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 3, 1.0, 0.3, 0.09, 0, 0, fake, fake,
+                           fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 1, -1.0, 0.3, 0.09, 0, 0, fake, fake,
+                           fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 0, 1.0, 0.3, 0.09, 0, 0, fake, fake,
+                           fake, fake, fake, 0, None) == ERR_WORKSPACE
+    # compaction: row size not a multiple of 16 bytes
+    assert L.medusa_kv_compact(fake, fake, fake, fake, fake, 1, 1, 10, 6, 2, 1, None) == ERR_UNSUPPORTED
+    assert b"16" in L.medusa_last_error()
+
+
+def test_workspace_queries_are_host_only_and_sized():
+    assert M.medusa_heads_workspace(1, 4096, 4, 1, M.BF16) >= 5 * 4096 * 2
+    assert M.medusa_heads_workspace(65, 4096, 0, 1, M.BF16) == 0
+    assert M.medusa_topk_workspace(16, 4, 32000, 10) > 0
+    assert M.medusa_accept_workspace(16, 65) >= 16 * 65 * 16
+    # the 7B batch-1 attention splits the prefix; the long-context batch-32 one does not
+    assert M.medusa_tree_attn_workspace(1, 65, 32, 32, 128, 2048 + 65, M.BF16) > 0
+    assert M.medusa_tree_attn_workspace(1, 11, 4, 4, 64, 139, M.F32) == 0
