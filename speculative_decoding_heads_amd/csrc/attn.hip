@@ -33,7 +33,6 @@
 
 namespace medusa {
 
-constexpr int kKT = 64;             // keys per tile
 constexpr int kMaxF32Keys = 16384;  // f32 kernel keeps scores in LDS
 
 __device__ __forceinline__ int xcd_remap(int b, int total) {
@@ -42,23 +41,59 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return x * q + min(x, r) + j;
 }
 
-template <int D, int RB>
-__global__ __launch_bounds__(256) void tree_attn_bf16(
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
+// lane j receives element (j % 4) of the 64-bit words addressed by lanes
+// 4*i + j/4, i = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(
+          (__attribute__((address_space(3))) char*)(uintptr_t)(const void*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+constexpr int kRB = 1;              // 16-row blocks per wave
+constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWG = 16 * kRB * kWaves;   // query rows per workgroup
+constexpr int kKT2 = 64;            // keys per tile
+
+// Tree attention, bf16.  Workgroup = (sequence b, kv head g, key partition,
+// group of 128 query rows); each of the 8 waves owns one 16-row block.  Small
+// per-wave state (one row block) lets two workgroups share a CU, so one
+// hides the other's load latency.
+//   * Each 64-key tile of K and V is loaded cooperatively (16-byte pieces,
+//     coalesced) into a double-buffered LDS tile, rows stored contiguously
+//     with 16-byte chunks XOR-swizzled by row, so that both the K fragment
+//     reads and the transposing V reads are free of bank conflicts.
+//   * S^T = K Q^T per 16-row block (keys are MFMA rows, query rows MFMA
+//     columns: a lane holds 4 keys x 1 query row).  The probabilities feed
+//     O^T = V^T P^T straight from the S^T accumulators; V^T fragments come
+//     from ds_read_b64_tr_b16 on the row-major V tile.  A row's softmax state
+//     and its output column therefore live in the same lane.
+//   * The running max is raised (O^T, l rescaled) only when a tile's max
+//     exceeds it by more than 2^8, so most tiles skip the rescale.
+//   * One barrier per tile: tile i+1 is written to the other LDS buffer while
+//     tile i is multiplied, and tile i+2's loads are in flight.
+//   * Key partitions write unnormalised partial outputs with (max, sum) in
+//     log2 units for attn_merge; with one partition O is written directly.
+template <int D>
+__global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seq_len,
     const uint64_t* __restrict__ anc, int anc_words, int T, int nq, int nkv, int Pmax,
     float scale_log2, int nsplit, int rowgroups, int tiles_per_split, uint16_t* __restrict__ O,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
-  constexpr int KS = D + 8;    // LDS row stride of K (elements): +16 B against bank conflicts
-  constexpr int VS = kKT + 8;  // LDS row stride of V^T
-  constexpr int DS = D / 32;   // MFMA steps over the head dim
-  constexpr int DB = D / 16;   // 16-wide blocks of the head dim
-  constexpr int KLOADS = D / 32;  // 16-byte K loads per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kKT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  constexpr int DS = D / 32;            // MFMA steps over the head dim (S^T)
+  constexpr int DB = D / 16;            // 16-wide head-dim blocks (O^T)
+  constexpr int CPR = D * 2 / 16;       // 16-byte chunks per K/V row
+  constexpr int SWZ = CPR - 1;
+  constexpr int PIECES = kKT2 * CPR / kThreads;  // chunks per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][kKT2 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][kKT2 * D];
+  __shared__ uint64_t anc_s[kMaxT * kMaxAncWords];
 
-  const int total = gridDim.x;
-  const int tile_id = xcd_remap(blockIdx.x, total);
+  const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
   const int rg = tile_id % rowgroups;
   const int rest = tile_id / rowgroups;
   const int split = rest % nsplit;
@@ -66,99 +101,84 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(
   const int b = bg / nkv, g = bg - b * nkv;
   const int G = nq / nkv;
   const int rows = T * G;
-  const int rows_pad = rowgroups * 64 * RB;
+  const int rows_pad = rowgroups * kRowsWG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int wrow0 = rg * kRowsWG + wave * 16 * kRB;
+  // row blocks of this wave holding at least one real row
+  const int nvb = max(0, min(kRB, (rows - wrow0 + 15) / 16));
 
   const int P = seq_len[b];
   const bool valid = P >= 0 && P + T <= Pmax;
   const int nkeys = valid ? P + T : 0;
-  const int ntiles = (nkeys + kKT - 1) / kKT;
+  const int ntiles = (nkeys + kKT2 - 1) / kKT2;
   const int t_begin = split * tiles_per_split;
   const int t_end = min(ntiles, t_begin + tiles_per_split);
   const int64_t kvbase = ((int64_t)b * nkv + g) * (int64_t)Pmax * D;
 
-  uint4 qf[RB][DS];
-  uint64_t aw[RB][kMaxAncWords];
-  f32x4 acc[RB][DB];
-  float m_run[RB], l_run[RB];
-  int row_id[RB];
+  for (int i = threadIdx.x; i < T * anc_words; i += kThreads)
+    anc_s[(i / anc_words) * kMaxAncWords + i % anc_words] = anc[i];
+
+  uint4 qf[kRB][DS];
+  int node[kRB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = rg * 64 * RB + wave * 16 * RB + rb * 16 + r16;
-    row_id[rb] = row;
-    const int rr = min(row, rows - 1);
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int rr = min(wrow0 + 16 * rb + r16, rows - 1);
     const int t = rr / G, hg = rr - t * G;
+    node[rb] = t;
     const uint16_t* qp = Q + (((int64_t)b * T + t) * nq + g * G + hg) * D + 8 * g4;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[rb][ds] = ldg16(qp + 32 * ds);
+  }
+  f32x4 acc[kRB][DB];
+  float m_run[kRB], l_run[kRB];
 #pragma unroll
-    for (int w = 0; w < kMaxAncWords; ++w) aw[rb][w] = w < anc_words ? anc[(int64_t)t * anc_words + w] : 0ull;
+  for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[rb] = -INFINITY;
     l_run[rb] = 0.f;
   }
 
-  // tile loaders: K rows (4 threads per key), V as (4 keys) x (8 dims) per thread
-  const int kkey = threadIdx.x >> 2, kpart = threadIdx.x & 3;
-  const int vkq = threadIdx.x & 15, vdc = threadIdx.x >> 4;
-  const bool vact = vdc < D / 8;
-  uint4 kr[KLOADS], vr[4];
+  uint4 kr[PIECES], vr[PIECES];
   auto load_tile = [&](int tile) {
-    const int key0 = tile * kKT;
-    const int kk = min(key0 + kkey, Pmax - 1);
-    const uint16_t* src = Kc + kvbase + (int64_t)kk * D + kpart * (D / 4);
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) kr[i] = ldg16(src + 8 * i);
-    if (vact) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int vk = min(key0 + 4 * vkq + i, Pmax - 1);
-        vr[i] = ldg16(Vc + kvbase + (int64_t)vk * D + 8 * vdc);
-      }
+    for (int i = 0; i < PIECES; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c / CPR, ch = c % CPR;
+      const int64_t off = kvbase + (int64_t)min(tile * kKT2 + row, Pmax - 1) * D + 8 * ch;
+      kr[i] = ldg16(Kc + off);
+      vr[i] = ldg16(Vc + off);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i)
-      *reinterpret_cast<uint4*>(&ks[kkey * KS + kpart * (D / 4) + 8 * i]) = kr[i];
-    if (vact) {
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sh = (j & 1) * 16;
-        const uint32_t e0 = (w0[j >> 1] >> sh) & 0xffffu, e1 = (w1[j >> 1] >> sh) & 0xffffu;
-        const uint32_t e2 = (w2[j >> 1] >> sh) & 0xffffu, e3 = (w3[j >> 1] >> sh) & 0xffffu;
-        uint2 pk;
-        pk.x = e0 | (e1 << 16);
-        pk.y = e2 | (e3 << 16);
-        *reinterpret_cast<uint2*>(&vt[(8 * vdc + j) * VS + 4 * vkq]) = pk;
-      }
+    for (int i = 0; i < PIECES; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c / CPR, ch = c % CPR;
+      const int dst = row * D + 8 * (ch ^ (row & SWZ));
+      *reinterpret_cast<uint4*>(&kbuf[buf][dst]) = kr[i];
+      *reinterpret_cast<uint4*>(&vbuf[buf][dst]) = vr[i];
     }
   };
-
-  if (t_begin < t_end) load_tile(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < t_end) load_tile(tile + 1);
-    const int key0 = tile * kKT;
-    const bool tree_tile = key0 + kKT > P;
+  auto compute = [&](int tile, int buf) {
+    const int key0 = tile * kKT2;
+    const bool tree_tile = key0 + kKT2 > P;
+    const uint16_t* kb_ = kbuf[buf];
+    const uint16_t* vb_ = vbuf[buf];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
+      if (rb >= nvb) break;
       f32x4 s[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* kp = &ks[(16 * kb + r16) * KS + 8 * g4];
+        const int krow = 16 * kb + r16;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-          s[kb] = mfma16x16x32(*reinterpret_cast<const uint4*>(kp + 32 * ds), qf[rb][ds], s[kb]);
+        for (int ds = 0; ds < DS; ++ds) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(kb_ + krow * D + 8 * ((4 * ds + g4) ^ (krow & SWZ)));
+          s[kb] = mfma16x16x32(kf, qf[rb][ds], s[kb]);
+        }
       }
       float x[4][4];
       float mt = -INFINITY;
@@ -170,66 +190,85 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(
           bool vis = key < P;
           if (tree_tile && !vis && key < nkeys) {
             const int j = key - P;
-            const uint64_t w = j < 64 ? aw[rb][0] : j < 128 ? aw[rb][1] : j < 192 ? aw[rb][2] : aw[rb][3];
-            vis = (w >> (j & 63)) & 1ull;
+            vis = (anc_s[node[rb] * kMaxAncWords + (j >> 6)] >> (j & 63)) & 1ull;
           }
           x[kb][i] = vis ? s[kb][i] * scale_log2 : -INFINITY;
           mt = fmaxf(mt, x[kb][i]);
         }
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[rb], mt);
-      float alpha = 1.f;
-      float psum = 0.f;
-      if (m_new != -INFINITY) {
-        alpha = exp2f(m_run[rb] - m_new);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[kb][i] = exp2f(x[kb][i] - m_new);
-            psum += x[kb][i];
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[kb][i] = 0.f;
-      }
-      m_run[rb] = m_new;
-      l_run[rb] = l_run[rb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[rb][db][0] *= alpha; acc[rb][db][1] *= alpha;
-        acc[rb][db][2] *= alpha; acc[rb][db][3] *= alpha;
-      }
-#pragma unroll
-      for (int kstep = 0; kstep < 2; ++kstep) {
-        uint4 pb;
-        pb.x = pack_bf16x2(x[2 * kstep][0], x[2 * kstep][1]);
-        pb.y = pack_bf16x2(x[2 * kstep][2], x[2 * kstep][3]);
-        pb.z = pack_bf16x2(x[2 * kstep + 1][0], x[2 * kstep + 1][1]);
-        pb.w = pack_bf16x2(x[2 * kstep + 1][2], x[2 * kstep + 1][3]);
+      // lazy max: raised only when the tile max exceeds it by more than 2^8
+      const bool raise = mt > m_run[rb] + 8.0f;
+      if (__any(raise)) {
+        const float m_new = raise ? mt : m_run[rb];
+        const float alpha = m_run[rb] == -INFINITY ? 0.f : exp2f(m_run[rb] - m_new);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vp = &vt[(16 * db + r16) * VS + 32 * kstep + 4 * g4];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+          acc[rb][db][0] *= alpha; acc[rb][db][1] *= alpha;
+          acc[rb][db][2] *= alpha; acc[rb][db][3] *= alpha;
+        }
+        l_run[rb] *= alpha;
+        m_run[rb] = m_new;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[kb][i] = x[kb][i] == -INFINITY ? 0.f : exp2f(x[kb][i] - m_run[rb]);
+          psum += x[kb][i];
+        }
+      l_run[rb] += psum;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 pb;   // P^T slots 8*g4 + j <-> keys 32*ks + 16*(j/4) + 4*g4 + j%4
+        pb.x = pack_bf16x2(x[2 * ks][0], x[2 * ks][1]);
+        pb.y = pack_bf16x2(x[2 * ks][2], x[2 * ks][3]);
+        pb.z = pack_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1]);
+        pb.w = pack_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3]);
+        // lane j of group g4 addresses V[32*ks + 4*g4 + j/4 (+16)][16*db + 4*(j%4) .. +4];
+        // the transposing read returns V[32*ks + 4*g4 + i (+16)][16*db + j], i = 0..3
+        const int vrow = 32 * ks + 4 * g4 + (r16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int cb = 32 * db + 8 * (r16 & 3);
+          const int ch = cb >> 4, he = (cb & 15) >> 1;
+          const uint2 lo = lds_read_tr16(vb_ + vrow * D + 8 * (ch ^ (vrow & SWZ)) + he);
+          const uint2 hi = lds_read_tr16(vb_ + (vrow + 16) * D + 8 * (ch ^ ((vrow + 16) & SWZ)) + he);
           uint4 va;
           va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
           acc[rb][db] = mfma16x16x32(va, pb, acc[rb][db]);
         }
       }
     }
+  };
+
+  __syncthreads();   // anc_s
+  if (t_begin < t_end) {
+    const int tl = t_end - 1;
+    load_tile(t_begin);
+    store_tile(0);
+    load_tile(min(t_begin + 1, tl));
+    __syncthreads();
+    for (int tile = t_begin; tile < t_end; ++tile) {
+      const int buf = (tile - t_begin) & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      compute(tile, buf);
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(buf ^ 1);                 // tile + 1 (a repeat of the last tile at the end)
+      load_tile(min(tile + 2, tl));
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
   }
 
   // epilogue
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     float l = l_run[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int row = row_id[rb];
+    const int row = wrow0 + 16 * rb + r16;
     if (row >= rows) continue;
     if (nsplit == 1) {
       const int t = row / G, hg = row - t * G;
@@ -355,16 +394,17 @@ AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
   if (dtype != kBF16) return p;
   const int G = nq / nkv;
   const int rows = T * G;
-  p.rb = rows > 64 ? 2 : 1;
-  p.rowgroups = (rows + 64 * p.rb - 1) / (64 * p.rb);
-  const int tiles = (Pmax + kKT - 1) / kKT;
+  p.rb = kRB;
+  p.rowgroups = (rows + kRowsWG - 1) / kRowsWG;
+  const int tiles = (Pmax + kKT2 - 1) / kKT2;
   const int base = b * nkv * p.rowgroups;
-  int want = (768 + base - 1) / base;
-  int maxsplit = tiles / 2 > 0 ? tiles / 2 : 1;
+  // aim at >= 512 workgroups, >= 4 tiles (256 keys) per partition
+  int want = (512 + base - 1) / base;
+  int maxsplit = tiles / 4 > 0 ? tiles / 4 : 1;
   p.nsplit = want < maxsplit ? want : maxsplit;
   if (p.nsplit < 1) p.nsplit = 1;
   if (p.nsplit > 1) {
-    const size_t rows_pad = (size_t)p.rowgroups * 64 * p.rb;
+    const size_t rows_pad = (size_t)p.rowgroups * kRowsWG;
     p.ws_bytes = (size_t)b * nkv * p.nsplit * rows_pad * ((size_t)d * sizeof(float) + sizeof(float2));
   }
   return p;
@@ -382,10 +422,10 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
     return hipGetLastError();
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  const int tiles = (Pmax + kKT - 1) / kKT;
+  const int tiles = (Pmax + kKT2 - 1) / kKT2;
   const int tps = (tiles + p.nsplit - 1) / p.nsplit;
   const int rows = T * (nq / nkv);
-  const int rows_pad = p.rowgroups * 64 * p.rb;
+  const int rows_pad = p.rowgroups * kRowsWG;
   float* ws_o = static_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + (size_t)b * nkv * p.nsplit * rows_pad * d * sizeof(float));
@@ -394,16 +434,14 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
   const uint16_t* k = static_cast<const uint16_t*>(Kc);
   const uint16_t* v = static_cast<const uint16_t*>(Vc);
   uint16_t* o = static_cast<uint16_t*>(O);
-#define ATTN(D_, RB_)                                                                          \
-  hipLaunchKernelGGL((tree_attn_bf16<D_, RB_>), dim3(nblk), dim3(256), 0, st, q, k, v, seq_len, \
-                     anc, anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit, p.rowgroups, tps, o, \
-                     ws_o, ws_ml)
-  if (d == 128) {
-    if (p.rb == 2) ATTN(128, 2); else ATTN(128, 1);
-  } else {
-    if (p.rb == 2) ATTN(64, 2); else ATTN(64, 1);
-  }
-#undef ATTN
+  if (d == 128)
+    hipLaunchKernelGGL(tree_attn_bf16<128>, dim3(nblk), dim3(kThreads), 0, st, q, k, v, seq_len, anc,
+                       anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit, p.rowgroups, tps, o, ws_o,
+                       ws_ml);
+  else
+    hipLaunchKernelGGL(tree_attn_bf16<64>, dim3(nblk), dim3(kThreads), 0, st, q, k, v, seq_len, anc,
+                       anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit, p.rowgroups, tps, o, ws_o,
+                       ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   if (d == 128)

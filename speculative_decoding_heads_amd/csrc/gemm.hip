@@ -102,7 +102,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
   const int r16 = lane & 15, g4 = lane >> 4;
   const int n0 = blockIdx.x * 16 * NB;
   const int nchunks = Kd >> 7;
-  const int c_begin = (nchunks * wave) >> 2, c_end = (nchunks * (wave + 1)) >> 2;
 
   const uint16_t* wp[NB];
   const uint16_t* xp[MB];
@@ -123,43 +122,56 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wa[NB][4], xb[MB][4];
-  if (c_begin < c_end) {
-    const int k0 = c_begin << 7;
+  // Two register stages used alternately (no copies between them), so the
+  // next chunk's loads stay in flight while the current chunk is multiplied.
+  uint4 wa[NB][4], xa[MB][4], wb[NB][4], xb[MB][4];
+  auto load = [&](int c, uint4 (&w)[NB][4], uint4 (&xv)[MB][4]) {
+    const int k0 = c << 7;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wa[nb][s] = ldg16_stream(wp[nb] + k0 + 8 * s);
+      for (int s = 0; s < 4; ++s) w[nb][s] = ldg16(wp[nb] + k0 + 8 * s);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xb[mb][s] = ldg16(xp[mb] + k0 + 8 * s);
-  }
-  for (int c = c_begin; c < c_end; ++c) {
-    const int kn = (c + 1 < c_end ? c + 1 : c) << 7;
-    uint4 wn[NB][4], xn[MB][4];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wn[nb][s] = ldg16_stream(wp[nb] + kn + 8 * s);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xn[mb][s] = ldg16(xp[mb] + kn + 8 * s);
+      for (int s = 0; s < 4; ++s) xv[mb][s] = ldg16(xp[mb] + k0 + 8 * s);
+  };
+  auto mma = [&](const uint4 (&w)[NB][4], const uint4 (&xv)[MB][4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16x16x32(wa[nb][s], xb[mb][s], acc[nb][mb]);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wa[nb][s] = wn[nb][s];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xb[mb][s] = xn[mb][s];
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16x16x32(w[nb][s], xv[mb][s], acc[nb][mb]);
+  };
+  // Waves take whole pairs of 128-wide chunks, so the two-stage body below has
+  // no branch: a load under a branch would make the compiler wait for every
+  // outstanding load before the next multiply (and it would sink the second
+  // stage's loads into that branch).  The next pair's first chunk is always
+  // prefetched (clamped at the end; a repeated chunk hits L2).  An odd last
+  // chunk is done on its own by wave 0.
+  const int npairs = nchunks >> 1;
+  const int p_begin = (npairs * wave) >> 2, p_end = (npairs * (wave + 1)) >> 2;
+  if (p_begin < p_end) {
+    const int c_last = 2 * p_end - 1;
+    load(2 * p_begin, wa, xa);
+    for (int c = 2 * p_begin; c < 2 * p_end; c += 2) {
+      // scheduling barriers keep each stage's loads issued before the other
+      // stage's multiplies (issue is in order: a load placed after a
+      // dependent MFMA chain would leave the memory pipe idle meanwhile)
+      load(c + 1, wb, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wa, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(c + 2, c_last), wa, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wb, xb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if ((nchunks & 1) && wave == 0) {
+    load(nchunks - 1, wb, xb);
+    mma(wb, xb);
   }
 
   // cross-wave reduction of the 4 K-partials
@@ -197,12 +209,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
   constexpr int BM = 16 * MB;
   constexpr int BN = 64 * NBW;
   constexpr int LDSROW = 128 + 8;              // bf16 elements per LDS row (16 B pad)
+  constexpr int XP = MB;                       // 16-byte X pieces per thread per chunk
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDSROW];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int total = gridDim.x;
-  const int t = xcd_tile(blockIdx.x, total);
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
   const int tm = t % ntm, tn = t / ntm;
   const int m0 = tm * BM, n0 = tn * BN + wave * 16 * NBW;
   const int nchunks = Kd >> 7;
@@ -213,16 +225,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
     int n = min(n0 + 16 * nb + r16, N - 1);
     wp[nb] = W + (int64_t)n * Kd + 32 * g4;
   }
-  // X tile loader: BM rows x 256 B per chunk = 16*BM pieces of 16 B
-  constexpr int XPIECES = BM * 16 / 256;       // per thread (= MB)
-  const uint16_t* xsrc[XPIECES];
-  int xdst[XPIECES];
+  const uint16_t* xsrc[XP];
+  int xdst[XP];
 #pragma unroll
-  for (int i = 0; i < XPIECES; ++i) {
-    int piece = threadIdx.x + 256 * i;
-    int row = piece >> 4, part = piece & 15;
-    int m = min(m0 + row, M - 1);
-    xsrc[i] = X + (int64_t)m * ldx + part * 8;
+  for (int i = 0; i < XP; ++i) {
+    const int piece = threadIdx.x + 256 * i;   // BM rows x 16 pieces
+    const int row = piece >> 4, part = piece & 15;
+    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + part * 8;
     xdst[i] = row * LDSROW + part * 8;
   }
 
@@ -232,47 +241,61 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wa[NBW][4], xr[XPIECES];
-#pragma unroll
-  for (int i = 0; i < XPIECES; ++i) xr[i] = ldg16(xsrc[i]);
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) wa[nb][s] = ldg16(wp[nb] + 8 * s);
-#pragma unroll
-  for (int i = 0; i < XPIECES; ++i) *reinterpret_cast<uint4*>(&xs[0][xdst[i]]) = xr[i];
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const int kn = (c + 1 < nchunks ? c + 1 : c) << 7;
-    uint4 wn[NBW][4];
-#pragma unroll
-    for (int i = 0; i < XPIECES; ++i) xr[i] = ldg16(xsrc[i] + kn);
+  uint4 wa[NBW][4], wb[NBW][4], xr[XP];
+  auto loadW = [&](int c, uint4 (&w)[NBW][4]) {
+    const int k0 = c << 7;
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wn[nb][s] = ldg16(wp[nb] + kn + 8 * s);
+      for (int s = 0; s < 4; ++s) w[nb][s] = ldg16(wp[nb] + k0 + 8 * s);
+  };
+  auto loadX = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) xr[i] = ldg16(xsrc[i] + (c << 7));
+  };
+  auto storeX = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) *reinterpret_cast<uint4*>(&xs[buf][xdst[i]]) = xr[i];
+  };
+  auto mma = [&](const uint4 (&w)[NBW][4], int buf) {
     const uint16_t* xb = &xs[buf][r16 * LDSROW + 32 * g4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * s);
+        const uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * s);
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[nb][mb] = mfma16x16x32(wa[nb][s], b, acc[nb][mb]);
+        for (int nb = 0; nb < NBW; ++nb) acc[nb][mb] = mfma16x16x32(w[nb][s], b, acc[nb][mb]);
       }
     }
-    if (c + 1 < nchunks) {
-#pragma unroll
-      for (int i = 0; i < XPIECES; ++i) *reinterpret_cast<uint4*>(&xs[buf ^ 1][xdst[i]]) = xr[i];
-    }
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wa[nb][s] = wn[nb][s];
+  };
+
+  // Chunk c uses LDS buffer c & 1.  Weights: two register stages used
+  // alternately (loads never under a branch, indices clamped); X: one chunk
+  // ahead in registers, written to the free LDS buffer after the multiply.
+  const int cl = nchunks - 1;
+  loadX(0);
+  loadW(0, wa);
+  storeX(0);
+  __syncthreads();
+  loadX(min(1, cl));
+  loadW(min(1, cl), wb);
+  for (int c = 0; c + 1 < nchunks; c += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wa, 0);
+    storeX(1);
+    loadX(min(c + 2, cl));
+    loadW(min(c + 2, cl), wa);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    mma(wb, 1);
+    storeX(0);
+    loadX(min(c + 3, cl));
+    loadW(min(c + 3, cl), wb);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
+  if (nchunks & 1) mma(wa, 0);
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -322,26 +345,32 @@ template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
                               int Kd, const Epi& epi, hipStream_t st) {
   const int mb = (M + 15) / 16;
-  if (M <= 80) {
-    // skinny: NB chosen so that the LDS reduction stays <= 64 KB
-#define SKINNY(NB_, MB_)                                                                     \
-  hipLaunchKernelGGL((gemm_skinny_bf16<NB_, MB_, Epi>), dim3((N + 16 * NB_ - 1) / (16 * NB_)), \
-                     dim3(256), 0, st, X, ldx, M, W, N, Kd, epi)
-    switch (mb) {
-      case 1: SKINNY(2, 1); break;
-      case 2: SKINNY(2, 2); break;
-      case 3: SKINNY(2, 3); break;
-      case 4: SKINNY(2, 4); break;
-      default: SKINNY(2, 5); break;
-    }
-#undef SKINNY
-  } else {
-    constexpr int MB = 8, NBW = 4;
-    const int ntm = (M + 16 * MB - 1) / (16 * MB);
-    const int ntn = (N + 64 * NBW - 1) / (64 * NBW);
-    hipLaunchKernelGGL((gemm_tiled_bf16<MB, NBW, Epi>), dim3(ntm * ntn), dim3(256), 0, st, X, ldx,
-                       M, W, N, Kd, ntm, epi);
+  if (mb == 1) {
+    // skinny: 4 waves split K, X (16 rows at most) read from L2
+    hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3((N + 31) / 32), dim3(256), 0, st, X, ldx,
+                       M, W, N, Kd, epi);
+    return hipGetLastError();
   }
+#define TILED(MB_, NBW_)                                                                       \
+  do {                                                                                         \
+    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
+    const int ntn = (N + 64 * NBW_ - 1) / (64 * NBW_);                                         \
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi>), dim3(ntm * ntn), dim3(256), 0, st, X, \
+                       ldx, M, W, N, Kd, ntm, epi);                                            \
+  } while (0)
+  switch (mb) {
+    case 2: TILED(2, 1); break;
+    case 3: TILED(3, 1); break;
+    case 4: TILED(4, 1); break;
+    case 5: TILED(5, 1); break;
+    case 6: TILED(6, 1); break;
+    case 7:
+    case 8: TILED(8, 1); break;
+    case 9:
+    case 10: TILED(10, 1); break;
+    default: TILED(8, 2); break;
+  }
+#undef TILED
   return hipGetLastError();
 }
 
