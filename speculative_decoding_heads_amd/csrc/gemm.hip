@@ -26,6 +26,8 @@
 //                 that the M-tiles of one weight tile run on one XCD (L2 reuse).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -302,6 +304,111 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
     for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 16 * nb + 4 * g4, acc[nb][mb]);
 }
 
+// ---------------------------------------------------------------- big-M bf16
+// MFMA-bound shape (hundreds to thousands of activation rows, e.g. the
+// verify rows of a batch).  Workgroup tile: BN = 32*WNB weight rows x
+// BM = 32*WMB activation rows; 2x2 waves, each 16*WNB x 16*WMB.  Both
+// operands are staged through double-buffered LDS in 64-wide K slices, rows
+// of 128 B with 16-byte chunks XOR-swizzled by (row >> 1) & 7 so the MFMA
+// fragment reads are free of bank conflicts.  One barrier per K slice; the
+// next slice is in registers while the current one is multiplied.
+template <int WMB, int WNB, class Epi>
+__global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict__ X, int64_t ldx,
+                                                     int M, const uint16_t* __restrict__ W, int N,
+                                                     int Kd, int ntm, Epi epi) {
+  constexpr int BM = 32 * WMB, BN = 32 * WNB, BK = 64;
+  constexpr int XP = BM * 8 / 256, WP = BN * 8 / 256;   // 16-byte pieces per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t wsm[2][BN * BK];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int tm = t % ntm, tn = t / ntm;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = Kd / BK;
+
+  const uint16_t* xsrc[XP];
+  const uint16_t* wsrc[WP];
+  int xdst[XP], wdst[WP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int p = threadIdx.x + 256 * i, row = p >> 3, ch = p & 7;
+    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch;
+    xdst[i] = row * BK + 8 * (ch ^ ((row >> 1) & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < WP; ++i) {
+    const int p = threadIdx.x + 256 * i, row = p >> 3, ch = p & 7;
+    wsrc[i] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ch;
+    wdst[i] = row * BK + 8 * (ch ^ ((row >> 1) & 7));
+  }
+  uint4 xr[XP], wr[WP];
+  auto load = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) xr[i] = ldg16(xsrc[i] + k0);
+#pragma unroll
+    for (int i = 0; i < WP; ++i) wr[i] = ldg16(wsrc[i] + k0);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) *reinterpret_cast<uint4*>(&xs[buf][xdst[i]]) = xr[i];
+#pragma unroll
+    for (int i = 0; i < WP; ++i) *reinterpret_cast<uint4*>(&wsm[buf][wdst[i]]) = wr[i];
+  };
+
+  f32x4 acc[WNB][WMB];
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 a[WNB], bx[WMB];
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int row = wn * 16 * WNB + 16 * nb + r16;
+        a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * ((4 * kk + g4) ^ ((row >> 1) & 7))]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) {
+        const int row = wm * 16 * WMB + 16 * mb + r16;
+        bx[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * ((4 * kk + g4) ^ ((row >> 1) & 7))]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = mfma16x16x32(a[nb], bx[mb], acc[nb][mb]);
+    }
+  };
+
+  const int kl = nk - 1;
+  load(0);
+  store(0);
+  load(min(1, kl));
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    store(buf ^ 1);                  // slice kt + 1 (a repeat of the last one at the end)
+    load(min(kt + 2, kl));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+      epi.store4(m0 + wm * 16 * WMB + 16 * mb + r16, n0 + wn * 16 * WNB + 16 * nb + 4 * g4,
+                 acc[nb][mb]);
+}
+
 // ---------------------------------------------------------------- f32
 // One wave per weight row n; lanes split K; M <= 64 rows, looped in groups of 8.
 template <class Epi>
@@ -358,6 +465,19 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi>), dim3(ntm * ntn), dim3(256), 0, st, X, \
                        ldx, M, W, N, Kd, ntm, epi);                                            \
   } while (0)
+  if (std::is_same<Epi, EpiLogits>::value && mb > 5 && (Kd % 64) == 0) {
+    // MFMA-bound: 256 weight rows x 224 or 256 activation rows per workgroup,
+    // whichever covers M with fewer padded rows
+    const int t7 = (M + 223) / 224, t8 = (M + 255) / 256;
+    const int ntn = (N + 255) / 256;
+    if (t7 * 224 < t8 * 256)
+      hipLaunchKernelGGL((gemm_big_bf16<7, 8, Epi>), dim3(t7 * ntn), dim3(256), 0, st, X, ldx, M, W,
+                         N, Kd, t7, epi);
+    else
+      hipLaunchKernelGGL((gemm_big_bf16<8, 8, Epi>), dim3(t8 * ntn), dim3(256), 0, st, X, ldx, M, W,
+                         N, Kd, t8, epi);
+    return hipGetLastError();
+  }
   switch (mb) {
     case 2: TILED(2, 1); break;
     case 3: TILED(3, 1); break;

@@ -81,7 +81,8 @@ def test_zero_head_weights_reduce_to_base_head_bitwise(dt):
     assert_rows_close(np64(logits[:, 0]), ref, TOL_BF16 if dt == "bf16" else TOL_F32, "base")
 
 
-@pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 2000), (11, 256, 4096)])
+@pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 2000), (11, 256, 4096),
+                                       (2080, 384, 1000), (300, 128, 777), (97, 512, 300)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
