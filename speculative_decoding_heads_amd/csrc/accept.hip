@@ -16,8 +16,8 @@
 // float64 sample from softmax(x / T) there (typical, counter draw 1).
 //
 // Kernels:
-//   accept_stats: one workgroup per (sequence, node) row of base logits; a
-//     single streaming pass with 16-byte loads.  Greedy: argmax key.  Typical:
+//   accept_stats: one 1024-thread workgroup per (sequence, node) row of base
+//     logits; a single streaming pass with 16-byte loads.  Greedy: argmax key.  Typical:
 //     online (m, s, t) with s = sum e^(x'-m), t = sum e^(x'-m)(x'-m),
 //     x' = x / T, rescaled whenever the running max moves; then
 //     H = ln s - t/s and log q(tok) = x'_tok - m - ln s.
@@ -70,61 +70,74 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& t, float m
   m = M;
 }
 
+constexpr int kStatThreads = 1024;
+
+// One 1024-thread workgroup per node row; each lane issues a group of 16-byte
+// loads before using any, then folds them into its argmax key (greedy) or its
+// online (m, s, t) state (typical); waves reduce by shuffles, LDS joins waves.
 template <int MODE>
-__global__ __launch_bounds__(256) void accept_stats(const float* __restrict__ logits, int V,
-                                                    float inv_temp, int* __restrict__ amax,
-                                                    Stat* __restrict__ stats) {
+__global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __restrict__ logits,
+                                                             int V, float inv_temp,
+                                                             int* __restrict__ amax,
+                                                             Stat* __restrict__ stats) {
   const int64_t row = blockIdx.x;
   const float* x = logits + row * V;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (MODE == kGreedy) {
-    uint64_t best = 0;
-    if ((V & 3) == 0) {
-      for (int e = 4 * tid; e < V; e += 1024) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(x + e);
+  constexpr int NW = kStatThreads / 64;
+  constexpr int U = 8;
+  uint64_t best = 0;
+  float m = -INFINITY, s = 0.f, t = 0.f;
+  auto take = [&](float v, int e) {
+    if (MODE == kGreedy) {
+      const uint64_t k = make_key(v, e);
+      best = k > best ? k : best;
+    } else {
+      stat_add(m, s, t, v * inv_temp);
+    }
+  };
+  if ((V & 3) == 0) {
+    const int nv = V >> 2;
+    for (int base = 0; base < nv; base += U * kStatThreads) {
+      f32x4 v[U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint64_t k = make_key(v[i], e + i);
-          best = k > best ? k : best;
+      for (int u = 0; u < U; ++u) {
+        const int e = base + u * kStatThreads + tid;
+        v[u] = e < nv ? *reinterpret_cast<const f32x4*>(x + 4 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = base + u * kStatThreads + tid;
+        if (e < nv) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) take(v[u][q], 4 * e + q);
         }
       }
-    } else {
-      for (int e = tid; e < V; e += 256) {
-        const uint64_t k = make_key(x[e], e);
-        best = k > best ? k : best;
-      }
     }
+  } else {
+    for (int e = tid; e < V; e += kStatThreads) take(x[e], e);
+  }
+  if (MODE == kGreedy) {
     best = wave_max_u64(best);
-    __shared__ uint64_t sb[4];
+    __shared__ uint64_t sb[NW];
     if (lane == 0) sb[wave] = best;
     __syncthreads();
     if (tid == 0) {
-      uint64_t b = sb[0];
-      for (int w = 1; w < 4; ++w) b = sb[w] > b ? sb[w] : b;
-      amax[row] = (int)key_index(b);
+      uint64_t bb = sb[0];
+      for (int w = 1; w < NW; ++w) bb = sb[w] > bb ? sb[w] : bb;
+      amax[row] = (int)key_index(bb);
     }
   } else {
-    float m = -INFINITY, s = 0.f, t = 0.f;
-    if ((V & 3) == 0) {
-      for (int e = 4 * tid; e < V; e += 1024) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(x + e);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stat_add(m, s, t, v[i] * inv_temp);
-      }
-    } else {
-      for (int e = tid; e < V; e += 256) stat_add(m, s, t, x[e] * inv_temp);
-    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), t2 = __shfl_xor(t, o, 64);
       stat_merge(m, s, t, m2, s2, t2);
     }
-    __shared__ float sm[4][3];
+    __shared__ float sm[NW][3];
     if (lane == 0) { sm[wave][0] = m; sm[wave][1] = s; sm[wave][2] = t; }
     __syncthreads();
     if (tid == 0) {
       float M = sm[0][0], S = sm[0][1], Tt = sm[0][2];
-      for (int w = 1; w < 4; ++w) stat_merge(M, S, Tt, sm[w][0], sm[w][1], sm[w][2]);
+      for (int w = 1; w < NW; ++w) stat_merge(M, S, Tt, sm[w][0], sm[w][1], sm[w][2]);
       stats[row] = Stat{M, S, Tt, 0.f};
     }
   }
@@ -226,14 +239,14 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   int* best = amax + rows;
   const float inv_temp = 1.0f / temperature;
   if (mode == kGreedy) {
-    hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(256), 0, st, base_logits,
+    hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
                        V, inv_temp, amax, stats);
     hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
                        parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
                        acc_tokens, bonus, best);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(256), 0, st, base_logits,
+  hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
                      V, inv_temp, amax, stats);
   hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
                      depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,

@@ -112,7 +112,8 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
 // ------------------------------------------------------------------- top-k
 size_t medusa_topk_workspace(int32_t b, int32_t K, int32_t V, int32_t kmax) {
   if (b <= 0 || K <= 0 || V <= 0 || kmax <= 0) return 0;
-  return round_up(topk_workspace(b, K, V, kmax));
+  const size_t n = topk_workspace(b, K, V, kmax);
+  return n ? round_up(n) : 0;
 }
 
 int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
@@ -133,7 +134,7 @@ int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int3
   if (!logits || !root || !idx || !val) return fail(MEDUSA_ERR_ARG, "NULL pointer");
   if ((int64_t)b * (K + 1) > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (K+1) > 65535");
   const size_t need = medusa_topk_workspace(b, K, V, kmax);
-  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
+  if (need && (!ws || ws_bytes < need)) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
   TopkArgs a{};
   a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
   a.temperature = temperature; a.seed = seed; a.step = step;

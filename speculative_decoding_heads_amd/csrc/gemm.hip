@@ -50,6 +50,7 @@ struct EpiLogits {
   __device__ __forceinline__ void store1(int m, int n, float v) const {
     if (m < M && n < N) C[(int64_t)m * ldc + n] = v;
   }
+  __device__ __forceinline__ void copy_base(int, int) const {}
 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
@@ -90,6 +91,16 @@ struct EpiHeads {
       }
     }
     for (int j = 0; j < 4; ++j) store1(m, n + j, v[j]);
+  }
+  // slot 0 of u is x itself (the base head): the workgroups whose weight rows
+  // fall in [0, H) also copy x[:, n_begin .. n_end) there.
+  __device__ __forceinline__ void copy_base(int n_begin, int n_end) const {
+    if (!base || n_begin >= H) return;
+    const int w = min(n_end, H) - n_begin;
+    for (int e = threadIdx.x; e < M * w; e += blockDim.x) {
+      const int m = e / w, o = n_begin + e - m * w;
+      U[(int64_t)m * R * H + o] = X[(int64_t)m * ldx + o];
+    }
   }
 };
 
@@ -193,6 +204,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
     const int nb = p / MB, mb = p - nb * MB;
     epi.store4(16 * mb + r16, n0 + 16 * nb + 4 * g4, v);
   }
+  epi.copy_base(n0, n0 + 16 * NB);
 }
 
 // ---------------------------------------------------------------- tiled bf16
@@ -302,6 +314,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 16 * nb + 4 * g4, acc[nb][mb]);
+  if (tm == 0) epi.copy_base(tn * BN, tn * BN + BN);
 }
 
 // ---------------------------------------------------------------- big-M bf16
@@ -508,7 +521,7 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
   if (dtype == kBF16) {
     const uint16_t* X = static_cast<const uint16_t*>(x);
     uint16_t* U = static_cast<uint16_t*>(u);
-    if (base) {
+    if (base && n_heads == 0) {
       int64_t tot = (int64_t)M * H;
       hipLaunchKernelGGL(copy_base_rows<uint16_t>, dim3((unsigned)((tot + 255) / 256)), dim3(256),
                          0, st, U, X, (int64_t)H, M, H, R);

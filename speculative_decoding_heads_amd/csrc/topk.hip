@@ -4,16 +4,7 @@
 // tree": keep the top k_i tokens of head i.  Order: logit descending, equal
 // logits by lower vocabulary index (a 64-bit key, see common.h).
 //
-// Selection is two launches:
-//   1. topk_chunk: grid (chunks, rows).  Each lane streams its slice of a
-//      vocabulary chunk with 16-byte loads and keeps a sorted register list of
-//      its KM best keys (a new key is compared with the list's last entry and
-//      usually rejected).  The 64 lists of a wave are merged by k rounds of a
-//      wave-wide max (shuffle butterfly) in which the lane holding the winner
-//      (found by ballot) pops its head; the 4 wave results are staged in LDS
-//      and merged by one wave the same way.
-//   2. topk_merge: one wave per row merges the chunk results (k rounds of
-//      "largest key below the previous pick") and writes indices and values.
+// Selection is one launch, one workgroup per row (see topk_rows).
 // The root row (head 0) takes k = 1 in greedy mode; in typical mode the root
 // is drawn by sample_rows instead.
 //
@@ -28,152 +19,184 @@
 
 namespace medusa {
 
-constexpr int kTopkChunk = 4096;   // vocabulary entries per workgroup in phase 1
-
-template <int KM>
-__device__ __forceinline__ void list_insert(uint64_t (&lst)[KM], uint64_t key) {
-  if (key <= lst[KM - 1]) return;
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    uint64_t hi = key > lst[j] ? key : lst[j];
-    uint64_t lo = key > lst[j] ? lst[j] : key;
-    lst[j] = hi;
-    key = lo;
-  }
-}
-
-// k rounds of wave max over the lanes' list heads; results in out[0..k).
-template <int KM>
-__device__ __forceinline__ void wave_merge_lists(uint64_t (&lst)[KM], int k, uint64_t* out) {
-  const int lane = threadIdx.x & 63;
-  for (int r = 0; r < k; ++r) {
-    uint64_t head = lst[0];
-    uint64_t best = wave_max_u64(head);
-    uint64_t mask = __ballot(head == best && best != 0);
-    int winner = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
-    if (lane == winner) {
-#pragma unroll
-      for (int j = 0; j < KM - 1; ++j) lst[j] = lst[j + 1];
-      lst[KM - 1] = 0;
-    }
-    if (lane == 0) out[r] = best;
-  }
-}
 
 __device__ __forceinline__ int row_k(const TopkArgs& a, int i) {
   if (i == 0) return a.root_mode == kGreedy ? 1 : 0;
   return a.k[i - 1];
 }
 
-template <int KM>
-__global__ __launch_bounds__(256) void topk_chunk(const float* __restrict__ logits, TopkArgs a,
-                                                  uint64_t* __restrict__ ws, int nchunks) {
-  const int row = blockIdx.y;                 // s*(K+1) + i
-  const int i = row % (a.K + 1);
-  const int k = row_k(a, i);
-  const int c = blockIdx.x;
-  uint64_t* out = ws + ((int64_t)row * nchunks + c) * KM;
-  if (k == 0) return;
-  const float* x = logits + (int64_t)row * a.V;
-  const int lo = c * kTopkChunk, hi = min(a.V, lo + kTopkChunk);
+// One workgroup (1024 threads) per row, threshold selection:
+//   A. lanes stream their slice of the row (16-byte loads, a group issued
+//      before use), form the 64-bit keys and keep them in registers (rows up
+//      to 32768 entries; longer rows are re-read from L2 in step C) with the
+//      lane's largest key;
+//   B. tau = the k-th largest of the 1024 lane maxima (k rounds of a block-wide
+//      max below the previous pick: shuffle butterflies + LDS).  The k largest
+//      lane maxima are k distinct entries, so the row's k-th largest key is
+//      >= tau: every top-k entry has key >= tau;
+//   C. lanes append their keys >= tau to an LDS candidate list (about k
+//      entries for continuous data);
+//   D. wave 0 takes the k largest candidates, in order.
+// If ties make the candidate list overflow its LDS capacity, step D instead
+// runs k rounds of "largest key below the previous pick" over the whole row.
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkKPT = 32;          // keys kept per lane (rows up to 32768 entries)
+constexpr int kTopkCand = 2048;       // LDS candidate capacity
 
-  uint64_t lst[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) lst[j] = 0;
-  if ((a.V & 3) == 0) {
-    for (int e = lo + 4 * threadIdx.x; e < hi; e += 4 * 256) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(x + e);
-      list_insert<KM>(lst, make_key(v[0], e));
-      list_insert<KM>(lst, make_key(v[1], e + 1));
-      list_insert<KM>(lst, make_key(v[2], e + 2));
-      list_insert<KM>(lst, make_key(v[3], e + 3));
-    }
-  } else {
-    for (int e = lo + threadIdx.x; e < hi; e += 256) list_insert<KM>(lst, make_key(x[e], e));
-  }
-  __shared__ uint64_t wres[4][KM];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  wave_merge_lists<KM>(lst, k, wres[wave]);
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = kTopkThreads / 64;
+  v = wave_max_u64(v);
   __syncthreads();
-  if (wave == 0) {
-    // lanes 0..4k-1 hold one candidate each
-    uint64_t one[KM];
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint64_t r = red[0];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) one[j] = 0;
-    if (lane < 4 * k) one[0] = wres[lane / k][lane % k];
-    uint64_t res[KM];
-    wave_merge_lists<KM>(one, k, res);
-    if (lane == 0)
-      for (int r = 0; r < KM; ++r) out[r] = r < k ? res[r] : 0;
-  }
+  for (int w = 1; w < NW; ++w) r = red[w] > r ? red[w] : r;
+  return r;
 }
 
-template <int KM>
-__global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ ws, TopkArgs a,
-                                                 int nchunks, int* __restrict__ root,
-                                                 int* __restrict__ idx, float* __restrict__ val) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restrict__ logits,
+                                                          TopkArgs a, int* __restrict__ root,
+                                                          int* __restrict__ idx,
+                                                          float* __restrict__ val) {
+  const int row = blockIdx.x;                 // s*(K+1) + i
   const int s = row / (a.K + 1), i = row % (a.K + 1);
   const int k = row_k(a, i);
-  const int lane = threadIdx.x;
-  const uint64_t* cand = ws + (int64_t)row * nchunks * KM;
-  const int ncand = nchunks * KM;
-  uint64_t prev = ~0ull;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-    for (int j = lane; j < ncand; j += 64) {
-      uint64_t v = cand[j];
-      if (v < prev && v > best) best = v;
-    }
-    best = wave_max_u64(best);
-    prev = best;
-    if (lane == 0) {
-      if (i == 0) {
-        root[s] = (int)key_index(best);
-      } else {
-        int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
-        idx[o] = (int)key_index(best);
-        val[o] = key_value(best);
-      }
-    }
-  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint64_t red[kTopkThreads / 64];
+  __shared__ uint64_t cand[kTopkCand];
+  __shared__ int ncand;
   if (i > 0) {
-    for (int r = k + lane; r < a.kmax; r += 64) {
-      int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
+    for (int r = k + tid; r < a.kmax; r += kTopkThreads) {
+      const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
       idx[o] = -1;
       val[o] = -INFINITY;
     }
   }
+  if (k == 0) return;
+  const float* x = logits + (int64_t)row * a.V;
+  const bool in_regs = (a.V & 3) == 0 && a.V <= kTopkKPT * kTopkThreads;
+
+  // ---- A: keys (in registers when the row fits) and the lane maximum
+  uint64_t keys[kTopkKPT];
+  uint64_t lmax = 0;
+  if (in_regs) {
+    const int nv = a.V >> 2;
+    f32x4 v[kTopkKPT / 4];
+#pragma unroll
+    for (int u = 0; u < kTopkKPT / 4; ++u) {
+      const int e = u * kTopkThreads + tid;
+      v[u] = e < nv ? *reinterpret_cast<const f32x4*>(x + 4 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kTopkKPT / 4; ++u) {
+      const int e = u * kTopkThreads + tid;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t kk = e < nv ? make_key(v[u][q], 4 * e + q) : 0ull;
+        keys[4 * u + q] = kk;
+        lmax = kk > lmax ? kk : lmax;
+      }
+    }
+  } else {
+    for (int e = tid; e < a.V; e += kTopkThreads) {
+      const uint64_t kk = make_key(x[e], e);
+      lmax = kk > lmax ? kk : lmax;
+    }
+  }
+  // ---- B: tau = k-th largest lane maximum
+  uint64_t prev = ~0ull, tau = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t mine = lmax < prev ? lmax : 0ull;
+    tau = block_max_u64(mine, red);
+    prev = tau;
+  }
+  // ---- C: candidates >= tau
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kTopkKPT; ++j) {
+      if (keys[j] >= tau && keys[j] != 0) {
+        const int slot = atomicAdd(&ncand, 1);
+        if (slot < kTopkCand) cand[slot] = keys[j];
+      }
+    }
+  } else {
+    for (int e = tid; e < a.V; e += kTopkThreads) {
+      const uint64_t kk = make_key(x[e], e);
+      if (kk >= tau) {
+        const int slot = atomicAdd(&ncand, 1);
+        if (slot < kTopkCand) cand[slot] = kk;
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = ncand;
+  // ---- D: the k largest candidates in order
+  if (nc <= kTopkCand) {
+    if (threadIdx.x < 64) {
+      uint64_t p = ~0ull;
+      for (int r = 0; r < k; ++r) {
+        uint64_t best = 0;
+        for (int j = lane; j < nc; j += 64) {
+          const uint64_t v = cand[j];
+          if (v < p && v > best) best = v;
+        }
+        best = wave_max_u64(best);
+        p = best;
+        if (lane == 0) {
+          if (i == 0) {
+            root[s] = (int)key_index(best);
+          } else {
+            const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
+            idx[o] = (int)key_index(best);
+            val[o] = key_value(best);
+          }
+        }
+      }
+    }
+  } else {
+    // overflow (heavy ties): k rounds over the whole row
+    uint64_t p = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+      if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < kTopkKPT; ++j)
+          if (keys[j] < p && keys[j] > best) best = keys[j];
+      } else {
+        for (int e = tid; e < a.V; e += kTopkThreads) {
+          const uint64_t kk = make_key(x[e], e);
+          if (kk < p && kk > best) best = kk;
+        }
+      }
+      best = block_max_u64(best, red);
+      p = best;
+      if (tid == 0) {
+        if (i == 0) {
+          root[s] = (int)key_index(best);
+        } else {
+          const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
+          idx[o] = (int)key_index(best);
+          val[o] = key_value(best);
+        }
+      }
+    }
+  }
 }
 
-static int km_for(int kmax) { return kmax <= 4 ? 4 : (kmax <= 8 ? 8 : 16); }
-
 size_t topk_workspace(int b, int K, int V, int kmax) {
-  const int nchunks = (V + kTopkChunk - 1) / kTopkChunk;
-  return (size_t)b * (K + 1) * nchunks * km_for(kmax) * sizeof(uint64_t);
+  (void)b; (void)K; (void)V; (void)kmax;
+  return 0;
 }
 
 hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
                     void* ws, hipStream_t st) {
-  const int nchunks = (a.V + kTopkChunk - 1) / kTopkChunk;
+  (void)ws;
   const int rows = a.b * (a.K + 1);
-  uint64_t* w = static_cast<uint64_t*>(ws);
-  dim3 g1(nchunks, rows);
-  switch (km_for(a.kmax)) {
-    case 4:
-      hipLaunchKernelGGL(topk_chunk<4>, g1, dim3(256), 0, st, logits, a, w, nchunks);
-      hipLaunchKernelGGL(topk_merge<4>, dim3(rows), dim3(64), 0, st, w, a, nchunks, root, idx, val);
-      break;
-    case 8:
-      hipLaunchKernelGGL(topk_chunk<8>, g1, dim3(256), 0, st, logits, a, w, nchunks);
-      hipLaunchKernelGGL(topk_merge<8>, dim3(rows), dim3(64), 0, st, w, a, nchunks, root, idx, val);
-      break;
-    default:
-      hipLaunchKernelGGL(topk_chunk<16>, g1, dim3(256), 0, st, logits, a, w, nchunks);
-      hipLaunchKernelGGL(topk_merge<16>, dim3(rows), dim3(64), 0, st, w, a, nchunks, root, idx,
-                         val);
-      break;
-  }
+  hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(kTopkThreads), 0, st, logits, a, root, idx, val);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.root_mode == kTypical)
