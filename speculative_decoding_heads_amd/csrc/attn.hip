@@ -292,6 +292,10 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
 }
 
 // Combine key partitions: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per (row, 4 dims); the loads of every partition are issued before
+// any is used (at most kMaxSplit partitions), then a single pass combines them.
+constexpr int kMaxSplit = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ ws_o,
                                                   const float2* __restrict__ ws_ml, int nsplit,
@@ -305,26 +309,38 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ ws_o
   if (row >= rows) return;
   const int b = bg / nkv, g = bg - b * nkv;
   const int G = nq / nkv;
+  const int64_t pbase = (int64_t)bg * nsplit * rows_pad + row;
+  float2 ml[kMaxSplit];
+  f32x4 o[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit) {
+      const int64_t prow = pbase + (int64_t)s * rows_pad;
+      ml[s] = ws_ml[prow];
+      o[s] = *reinterpret_cast<const f32x4*>(ws_o + prow * D + c);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((int64_t)bg * nsplit + s) * rows_pad + row].x);
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < nsplit) M = fmaxf(M, ml[s].x);
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t prow = ((int64_t)bg * nsplit + s) * rows_pad + row;
-    const float2 ml = ws_ml[prow];
-    if (ml.x == -INFINITY) continue;
-    const float w = exp2f(ml.x - M);
-    den += w * ml.y;
-    const f32x4 o = *reinterpret_cast<const f32x4*>(ws_o + prow * D + c);
-    num[0] += w * o[0]; num[1] += w * o[1]; num[2] += w * o[2]; num[3] += w * o[3];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit && ml[s].x != -INFINITY) {
+      const float w = exp2f(ml[s].x - M);
+      den += w * ml[s].y;
+      num[0] += w * o[s][0]; num[1] += w * o[s][1]; num[2] += w * o[s][2]; num[3] += w * o[s][3];
+    }
   }
   const float inv = 1.0f / den;
   const int t = row / G, hg = row - t * G;
   uint16_t* op = O + (((int64_t)b * T + t) * nq + g * G + hg) * D + c;
-  uint2 o;
-  o.x = pack_bf16x2(num[0] * inv, num[1] * inv);
-  o.y = pack_bf16x2(num[2] * inv, num[3] * inv);
-  *reinterpret_cast<uint2*>(op) = o;
+  uint2 r;
+  r.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+  r.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+  *reinterpret_cast<uint2*>(op) = r;
 }
 
 // ---------------------------------------------------------------- f32
@@ -400,8 +416,9 @@ AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
   const int base = b * nkv * p.rowgroups;
   // aim at >= 512 workgroups, >= 4 tiles (256 keys) per partition
   int want = (512 + base - 1) / base;
-  int maxsplit = tiles / 4 > 0 ? tiles / 4 : 1;
+  int maxsplit = tiles / 2 > 0 ? tiles / 2 : 1;
   p.nsplit = want < maxsplit ? want : maxsplit;
+  if (p.nsplit > kMaxSplit) p.nsplit = kMaxSplit;
   if (p.nsplit < 1) p.nsplit = 1;
   if (p.nsplit > 1) {
     const size_t rows_pad = (size_t)p.rowgroups * kRowsWG;

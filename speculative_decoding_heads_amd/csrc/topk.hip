@@ -30,10 +30,11 @@ __device__ __forceinline__ int row_k(const TopkArgs& a, int i) {
 //      before use), form the 64-bit keys and keep them in registers (rows up
 //      to 32768 entries; longer rows are re-read from L2 in step C) with the
 //      lane's largest key;
-//   B. tau = the k-th largest of the 1024 lane maxima (k rounds of a block-wide
-//      max below the previous pick: shuffle butterflies + LDS).  The k largest
-//      lane maxima are k distinct entries, so the row's k-th largest key is
-//      >= tau: every top-k entry has key >= tau;
+//   B. tau = the k-th largest of the 1024 lane maxima: each wave takes its k
+//      largest lane maxima (k rounds of a wave max below the previous pick,
+//      shuffle butterflies, no barrier), wave 0 takes the k-th largest of the
+//      16 x k results.  The k largest lane maxima are k distinct entries, so
+//      the row's k-th largest key is >= tau: every top-k entry has key >= tau;
 //   C. lanes append their keys >= tau to an LDS candidate list (about k
 //      entries for continuous data);
 //   D. wave 0 takes the k largest candidates, in order.
@@ -105,13 +106,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       lmax = kk > lmax ? kk : lmax;
     }
   }
-  // ---- B: tau = k-th largest lane maximum
-  uint64_t prev = ~0ull, tau = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint64_t mine = lmax < prev ? lmax : 0ull;
-    tau = block_max_u64(mine, red);
-    prev = tau;
+  // ---- B: tau = k-th largest lane maximum: each wave finds its k largest
+  // lane maxima (wave-local rounds), wave 0 takes the k-th largest of those
+  __shared__ uint64_t wtop[kTopkThreads / 64][kMaxK];
+  __shared__ uint64_t tau_s;
+  {
+    const int wave = tid >> 6;
+    uint64_t p = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      const uint64_t b_ = wave_max_u64(lmax < p ? lmax : 0ull);
+      p = b_;
+      if (lane == 0) wtop[wave][r] = b_;
+    }
   }
+  __syncthreads();
+  if (tid < 64) {
+    constexpr int NW = kTopkThreads / 64;
+    uint64_t p = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t b_ = 0;
+      for (int j = lane; j < NW * k; j += 64) {
+        const uint64_t v = wtop[j / k][j % k];
+        if (v < p && v > b_) b_ = v;
+      }
+      p = wave_max_u64(b_);
+    }
+    if (lane == 0) tau_s = p;
+  }
+  __syncthreads();
+  const uint64_t tau = tau_s;
   // ---- C: candidates >= tau
   if (tid == 0) ncand = 0;
   __syncthreads();
