@@ -16,14 +16,17 @@
 // consecutive n of one output row (one 16-byte store of logits).
 //
 // Two bf16 kernels:
-//   gemm_skinny : M <= 80.  HBM-bound weight stream.  A workgroup owns 16*NB
+//   gemm_skinny : M <= 8.  HBM-bound weight stream.  A workgroup owns 16*NB
 //                 weight rows; its 4 waves split K and reduce through LDS.
 //                 Both operands go global -> registers (X is tiny and stays in
 //                 L2); each lane loads 64 contiguous bytes per row per step.
-//   gemm_tiled  : larger M.  A workgroup owns BM = 16*MB activation rows
-//                 (staged in LDS, shared by its 4 waves) and 64*NBW weight rows
-//                 (16*NBW per wave, direct loads).  Tiles are mapped to XCDs so
-//                 that the M-tiles of one weight tile run on one XCD (L2 reuse).
+//   gemm_tiled  : 8 < M <= 80 (and heads with larger M).  A workgroup of 8
+//                 waves owns BM = 16*MB activation rows (staged in LDS once per
+//                 K chunk and shared by all waves: re-reading X per wave from
+//                 L2 costs more than the weights) and 128*NBW weight rows (16*NBW
+//                 per wave, direct loads).  Tiles are mapped to XCDs so that the
+//                 M-tiles of one weight tile run on one XCD (L2 reuse).
+//   gemm_big    : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
 #include <type_traits>
@@ -216,14 +219,16 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
   return x * q + min(x, r) + j;
 }
 
-template <int MB, int NBW, class Epi>
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restrict__ X, int64_t ldx,
-                                                       int M, const uint16_t* __restrict__ W,
-                                                       int N, int Kd, int ntm, Epi epi) {
+template <int MB, int NBW, class Epi, int NWAVES = 4>
+__global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* __restrict__ X,
+                                                               int64_t ldx, int M,
+                                                               const uint16_t* __restrict__ W,
+                                                               int N, int Kd, int ntm, Epi epi) {
+  constexpr int NT = 64 * NWAVES;
   constexpr int BM = 16 * MB;
-  constexpr int BN = 64 * NBW;
+  constexpr int BN = 16 * NBW * NWAVES;
   constexpr int LDSROW = 128 + 8;              // bf16 elements per LDS row (16 B pad)
-  constexpr int XP = MB;                       // 16-byte X pieces per thread per chunk
+  constexpr int XP = (BM * 16 + NT - 1) / NT;  // 16-byte X pieces per thread per chunk
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDSROW];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const uint16_t* __restric
   int xdst[XP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
-    const int piece = threadIdx.x + 256 * i;   // BM rows x 16 pieces
+    const int piece = min(threadIdx.x + NT * i, BM * 16 - 1);   // BM rows x 16 pieces
     const int row = piece >> 4, part = piece & 15;
     xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + part * 8;
     xdst[i] = row * LDSROW + part * 8;
@@ -465,20 +470,20 @@ template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
                               int Kd, const Epi& epi, hipStream_t st) {
   const int mb = (M + 15) / 16;
-  if (mb == 1) {
-    // skinny: 4 waves split K, X (16 rows at most) read from L2
+  if (M <= 8 || (!std::is_same<Epi, EpiLogits>::value && M <= 16)) {
+    // skinny: 4 waves split K, X (a few rows) read from L2
     hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3((N + 31) / 32), dim3(256), 0, st, X, ldx,
                        M, W, N, Kd, epi);
     return hipGetLastError();
   }
-#define TILED(MB_, NBW_)                                                                       \
-  do {                                                                                         \
-    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
-    const int ntn = (N + 64 * NBW_ - 1) / (64 * NBW_);                                         \
-    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi>), dim3(ntm * ntn), dim3(256), 0, st, X, \
-                       ldx, M, W, N, Kd, ntm, epi);                                            \
+#define TILED(MB_, NBW_)                                                                        \
+  do {                                                                                          \
+    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                            \
+    const int ntn = (N + 128 * NBW_ - 1) / (128 * NBW_);                                        \
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 8>), dim3(ntm * ntn), dim3(512), 0, st, \
+                       X, ldx, M, W, N, Kd, ntm, epi);                                          \
   } while (0)
-  if (std::is_same<Epi, EpiLogits>::value && mb > 5 && (Kd % 64) == 0) {
+  if constexpr (std::is_same<Epi, EpiLogits>::value) if (mb > 5 && (Kd % 64) == 0) {
     // MFMA-bound: 256 weight rows x 224 or 256 activation rows per workgroup,
     // whichever covers M with fewer padded rows
     const int t7 = (M + 223) / 224, t8 = (M + 255) / 256;
@@ -492,6 +497,7 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     return hipGetLastError();
   }
   switch (mb) {
+    case 1: TILED(1, 1); break;
     case 2: TILED(2, 1); break;
     case 3: TILED(3, 1); break;
     case 4: TILED(4, 1); break;
@@ -501,7 +507,7 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     case 8: TILED(8, 1); break;
     case 9:
     case 10: TILED(10, 1); break;
-    default: TILED(8, 2); break;
+    default: TILED(8, 1); break;
   }
 #undef TILED
   return hipGetLastError();
