@@ -30,7 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import hashlib
+
 METRIC = "Medusa verify steps/sec at 7B shape (bs1, bs16) + % of HBM/MFMA roofline"
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 CALLS = ["draft_heads", "topk", "build_tree", "tree_attn", "verify_lm", "accept", "kv_compact"]
@@ -163,11 +166,43 @@ def cpu_baseline(cfg, seconds, log=print):
         done += 1
         el = time.perf_counter() - t0
         log(f"[bench] oracle step {done}: {el:.1f}s")
-        if el >= seconds or done >= 20:
+        if el >= seconds or done >= 100:
             break
     return {"value": done / el, "unit": "verify-steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} full step(s) of the {c.name} workload, float64 numpy, "
                       f"{el:.1f} s wall"}
+
+
+def kernel_source_hash(name):
+    path = os.path.join(ROOT, "speculative_decoding_heads_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per launch of a call's kernel from the committed counter summary
+    (two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a copy of
+    known size), or None when absent or when the kernel source has changed."""
+    path = os.path.join(PROFILES, f"traffic_{call}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_hash(t["source"]):
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def copy_calibration(mib):
+    """One device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -181,6 +216,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -192,6 +229,8 @@ def main():
     from speculative_decoding_heads_amd import configs as C
 
     log = lambda m: print(m, file=sys.stderr, flush=True)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
     cfg = C.BY_NAME[args.workload]
     ms, per_call = measure(cfg, args.steps, args.warmup, args.rotate, log)
     value = 1000.0 / ms
@@ -210,7 +249,7 @@ def main():
                 "unit": "GB/s", "frac": round(bytes_rate / HBM_PEAK_GBPS, 4)}
     roof.update({"kernel": dom, "alg_bytes_per_launch": ab[dom],
                  "alg_flops_per_launch": af.get(dom, 0), "avg_launch_us": round(per_call[dom], 2),
-                 "traffic": None})
+                 "traffic": measured_traffic(cfg.name, dom)})
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "verify-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -65,13 +65,52 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
+// 64-bit wave max with DPP row operations instead of LDS-routed shuffles:
+// quad xor 1, quad xor 2, half-row mirror and row mirror leave every lane of a
+// 16-lane row with the row max; row broadcasts 15 and 31 fold rows into lane 63,
+// which is then read as a scalar.  The result is the same in every lane.
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, int ctrl_id) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t tlo, thi;
+  switch (ctrl_id) {
+    case 0:  // quad_perm [1,0,3,2]
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xF, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xF, 0xF, false);
+      break;
+    case 1:  // quad_perm [2,3,0,1]
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xF, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xF, 0xF, false);
+      break;
+    case 2:  // row_half_mirror
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xF, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xF, 0xF, false);
+      break;
+    case 3:  // row_mirror
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xF, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xF, 0xF, false);
+      break;
+    case 4:  // row_bcast15 into rows 1 and 3
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0x142, 0xA, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0x142, 0xA, 0xF, false);
+      break;
+    default:  // row_bcast31 into rows 2 and 3
+      tlo = __builtin_amdgcn_update_dpp(lo, lo, 0x143, 0xC, 0xF, false);
+      thi = __builtin_amdgcn_update_dpp(hi, hi, 0x143, 0xC, 0xF, false);
+      break;
   }
-  return v;
+  const uint64_t t = ((uint64_t)thi << 32) | tlo;
+  return t > v ? t : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step(v, 0);
+  v = dpp_max_step(v, 1);
+  v = dpp_max_step(v, 2);
+  v = dpp_max_step(v, 3);
+  v = dpp_max_step(v, 4);
+  v = dpp_max_step(v, 5);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---- order-preserving key for (value desc, index asc) selection ---------------
