@@ -10,16 +10,19 @@
 // bf16 kernel (gfx950 MFMA 16x16x32):
 //   * One workgroup = one (sequence, kv head, key partition, row group).  The
 //     query rows of a kv head are all (node, q head of the group) pairs, so a
-//     KV tile brought into LDS serves every tree node and every grouped head.
-//   * Per 64-key tile: K is stored row-major in LDS, V transposed (V^T).
-//     Each wave computes S^T = K Q^T for its 16-row blocks (the query rows are
+//     KV tile brought into LDS serves every tree node and every grouped head;
+//     a row group holds up to 384 rows, so grouped-query heads normally need
+//     one workgroup per KV tile.
+//   * K/V tiles stream through a 4-deep LDS ring filled by direct
+//     global->LDS loads (three tiles in flight per workgroup).
+//   * Each wave computes S^T = K Q^T for its 16-row blocks (the query rows are
 //     the MFMA columns), so a lane holds 4 keys x 1 query row: the online
 //     softmax state of a row lives in the lane that owns it, the probabilities
 //     feed the next MFMA (O^T = V^T P^T) straight from registers, and O^T
 //     comes out with the same row-per-lane layout, so the rescale by the
 //     running max is a per-lane multiply.
-//   * The ancestor bitmask (<= 4 words for <= 256 nodes) sits in registers;
-//     only keys >= P consult it.
+//   * The ancestor bitmask (<= 4 words per node) sits in LDS; only keys >= P
+//     consult it.
 //   * Key partitions ("split-KV") write unnormalised partial outputs with
 //     their (max, sum) in log2 units; attn_merge combines them.  With a single
 //     partition the kernel normalises and writes O directly.
@@ -52,32 +55,49 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-constexpr int kRB = 1;              // 16-row blocks per wave
+// LDS DMA (gfx950 global_load_lds_dwordx4): each lane's 16 bytes from its own
+// global address land at LDS byte m0 + 16 * lane.  The compiler does not see
+// this write: the caller waits with vm_wait<N>() and a barrier before any
+// wave reads the destination.  M0 is set in the same statement, one wait state
+// ahead of its use.  The 64-bit address register is consumed at issue.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 constexpr int kWaves = 8;           // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsWG = 16 * kRB * kWaves;   // query rows per workgroup
 constexpr int kKT2 = 64;            // keys per tile
+constexpr int kNBuf = 4;            // LDS ring depth in tiles
 
 // Tree attention, bf16.  Workgroup = (sequence b, kv head g, key partition,
-// group of 128 query rows); each of the 8 waves owns one 16-row block.  Small
-// per-wave state (one row block) lets two workgroups share a CU, so one
-// hides the other's load latency.
-//   * Each 64-key tile of K and V is loaded cooperatively (16-byte pieces,
-//     coalesced) into a double-buffered LDS tile, rows stored contiguously
-//     with 16-byte chunks XOR-swizzled by row, so that both the K fragment
-//     reads and the transposing V reads are free of bank conflicts.
+// group of 128*RB query rows); 8 waves, each owning RB 16-row blocks
+// (block rb of wave w is row block 8*rb + w of the group, so short groups
+// spread over all waves).
+//   * K and V tiles of 64 keys stream through a 4-deep LDS ring by direct
+//     global->LDS loads: three tiles are in flight while one is multiplied,
+//     with no staging registers.  Rows are stored contiguously with 16-byte
+//     chunks XOR-swizzled by row, so both the K fragment reads and the
+//     transposing V reads are free of bank conflicts.  One barrier per tile.
 //   * S^T = K Q^T per 16-row block (keys are MFMA rows, query rows MFMA
-//     columns: a lane holds 4 keys x 1 query row).  The probabilities feed
-//     O^T = V^T P^T straight from the S^T accumulators; V^T fragments come
-//     from ds_read_b64_tr_b16 on the row-major V tile.  A row's softmax state
-//     and its output column therefore live in the same lane.
+//     columns: a lane holds 4 keys x 1 query row); each K fragment read from
+//     LDS serves all RB row blocks.  The probabilities feed O^T = V^T P^T
+//     straight from the S^T accumulators; V^T fragments come from
+//     ds_read_b64_tr_b16 on the row-major V tile and also serve all RB blocks.
+//     A row's softmax state and its output column live in the same lane.
 //   * The running max is raised (O^T, l rescaled) only when a tile's max
 //     exceeds it by more than 2^8, so most tiles skip the rescale.
-//   * One barrier per tile: tile i+1 is written to the other LDS buffer while
-//     tile i is multiplied, and tile i+2's loads are in flight.
 //   * Key partitions write unnormalised partial outputs with (max, sum) in
 //     log2 units for attn_merge; with one partition O is written directly.
-template <int D>
+template <int D, int RB>
 __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seq_len,
@@ -88,9 +108,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   constexpr int DB = D / 16;            // 16-wide head-dim blocks (O^T)
   constexpr int CPR = D * 2 / 16;       // 16-byte chunks per K/V row
   constexpr int SWZ = CPR - 1;
-  constexpr int PIECES = kKT2 * CPR / kThreads;  // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][kKT2 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][kKT2 * D];
+  constexpr int ROWS_KB = 1024 / (2 * D);          // K/V rows per 1 KB DMA region
+  constexpr int NI = kKT2 / ROWS_KB / kWaves;      // DMA issues per thread per tensor per tile
+  constexpr int ROWS_WG = 16 * RB * kWaves;
+  static_assert(NI >= 1 && kKT2 % (ROWS_KB * kWaves) == 0, "tile must split into DMA regions");
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[kNBuf][kKT2 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kNBuf][kKT2 * D];
   __shared__ uint64_t anc_s[kMaxT * kMaxAncWords];
 
   const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
@@ -101,174 +124,194 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   const int b = bg / nkv, g = bg - b * nkv;
   const int G = nq / nkv;
   const int rows = T * G;
-  const int rows_pad = rowgroups * kRowsWG;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows_pad = rowgroups * ROWS_WG;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int wrow0 = rg * kRowsWG + wave * 16 * kRB;
-  // row blocks of this wave holding at least one real row
-  const int nvb = max(0, min(kRB, (rows - wrow0 + 15) / 16));
+  int blk[RB];
+  int nvb = 0;   // row blocks of this wave holding at least one real row
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    blk[rb] = rg * kWaves * RB + kWaves * rb + wave;
+    if (blk[rb] * 16 < rows) nvb = rb + 1;
+  }
 
   const int P = seq_len[b];
   const bool valid = P >= 0 && P + T <= Pmax;
   const int nkeys = valid ? P + T : 0;
   const int ntiles = (nkeys + kKT2 - 1) / kKT2;
   const int t_begin = split * tiles_per_split;
-  const int t_end = min(ntiles, t_begin + tiles_per_split);
+  const int nt = max(0, min(ntiles, t_begin + tiles_per_split) - t_begin);
   const int64_t kvbase = ((int64_t)b * nkv + g) * (int64_t)Pmax * D;
 
-  for (int i = threadIdx.x; i < T * anc_words; i += kThreads)
-    anc_s[(i / anc_words) * kMaxAncWords + i % anc_words] = anc[i];
-
-  uint4 qf[kRB][DS];
-  int node[kRB];
+  // DMA issue j of this thread fills 1 KB region j*8 + wave of a tile: rows
+  // ROWS_KB*region + lane/CPR, LDS chunk lane%CPR <- global chunk (lane%CPR) ^ (row & SWZ).
+  int drow[NI], dcol[NI];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int rr = min(wrow0 + 16 * rb + r16, rows - 1);
+  for (int j = 0; j < NI; ++j) {
+    drow[j] = (j * kWaves + wave) * ROWS_KB + lane / CPR;
+    dcol[j] = 8 * ((lane % CPR) ^ (drow[j] & SWZ));
+  }
+  const uint32_t klds = lds_u32(&kbuf[0][0]), vlds = lds_u32(&vbuf[0][0]);
+  auto issue = [&](int tile, int buf) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t off = kvbase + (int64_t)min(tile * kKT2 + drow[j], Pmax - 1) * D + dcol[j];
+      const uint32_t reg = (uint32_t)(buf * kKT2 * D * 2 + (j * kWaves + wave) * 1024);
+      dma16(Kc + off, __builtin_amdgcn_readfirstlane(klds + reg));
+      dma16(Vc + off, __builtin_amdgcn_readfirstlane(vlds + reg));
+    }
+  };
+
+  // the first tiles go out before anything else
+#pragma unroll
+  for (int i = 0; i < kNBuf - 1; ++i)
+    if (i < nt) issue(t_begin + i, i);
+
+  uint4 qf[RB][DS];
+  int node[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = min(blk[rb] * 16 + r16, rows - 1);
     const int t = rr / G, hg = rr - t * G;
     node[rb] = t;
     const uint16_t* qp = Q + (((int64_t)b * T + t) * nq + g * G + hg) * D + 8 * g4;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[rb][ds] = ldg16(qp + 32 * ds);
   }
-  f32x4 acc[kRB][DB];
-  float m_run[kRB], l_run[kRB];
+  for (int i = threadIdx.x; i < T * anc_words; i += kThreads)
+    anc_s[(i / anc_words) * kMaxAncWords + i % anc_words] = anc[i];
+  // every ordinary load (Q, ancestors) has landed: vmcnt(0), as the compiler
+  // sees it, so no wait for Q is placed inside the tile loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  f32x4 acc[RB][DB];
+  float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[rb] = -INFINITY;
     l_run[rb] = 0.f;
   }
 
-  uint4 kr[PIECES], vr[PIECES];
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c / CPR, ch = c % CPR;
-      const int64_t off = kvbase + (int64_t)min(tile * kKT2 + row, Pmax - 1) * D + 8 * ch;
-      kr[i] = ldg16(Kc + off);
-      vr[i] = ldg16(Vc + off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c / CPR, ch = c % CPR;
-      const int dst = row * D + 8 * (ch ^ (row & SWZ));
-      *reinterpret_cast<uint4*>(&kbuf[buf][dst]) = kr[i];
-      *reinterpret_cast<uint4*>(&vbuf[buf][dst]) = vr[i];
-    }
-  };
+  // One tile in two halves of 32 keys (ks): S^T for the half, its softmax
+  // update, then its share of O^T.  Halves keep the S^T accumulators of all RB
+  // blocks small enough to live beside O^T.  Tiles wholly inside the prefix
+  // (every key visible) take the unmasked path; the few tiles that reach the
+  // tree slots or the end of the keys apply the ancestor mask.
+  //   Softmax: each lane checks its own scores against the running max m (in
+  //   log2 units); only when some lane exceeds m + 8 are the row maxima formed
+  //   across the 4 lanes of a row and m raised (O^T and l rescaled), so the
+  //   common path has no cross-lane traffic.  p = 2^(s*scale - m) <= 2^8.
   auto compute = [&](int tile, int buf) {
     const int key0 = tile * kKT2;
-    const bool tree_tile = key0 + kKT2 > P;
+    const bool masked = key0 + kKT2 > P;   // uniform: tile reaches the tree slots
     const uint16_t* kb_ = kbuf[buf];
     const uint16_t* vb_ = vbuf[buf];
+#pragma unroll 1
+    for (int ks = 0; ks < 2; ++ks) {
+      f32x4 s[RB][2];
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      if (rb >= nvb) break;
-      f32x4 s[4];
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int krow = 16 * kb + r16;
+        for (int rb = 0; rb < RB; ++rb) s[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int krow = 32 * ks + 16 * h + r16;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
           const uint4 kf = *reinterpret_cast<const uint4*>(kb_ + krow * D + 8 * ((4 * ds + g4) ^ (krow & SWZ)));
-          s[kb] = mfma16x16x32(kf, qf[rb][ds], s[kb]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[rb][h] = mfma16x16x32(kf, qf[rb][ds], s[rb][h]);
         }
       }
-      float x[4][4];
-      float mt = -INFINITY;
+      uint4 pb[RB];   // P^T slots 8*g4 + j <-> keys 32*ks + 16*(j/4) + 4*g4 + j%4
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int rb = 0; rb < RB; ++rb) {
+        if (masked) {   // hidden scores become -inf, whose 2^x is 0
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * kb + 4 * g4 + i;
-          bool vis = key < P;
-          if (tree_tile && !vis && key < nkeys) {
-            const int j = key - P;
-            vis = (anc_s[node[rb] * kMaxAncWords + (j >> 6)] >> (j & 63)) & 1ull;
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 32 * ks + 16 * h + 4 * g4 + i;
+              const int j = key - P;
+              const bool in_tree = (unsigned)j < (unsigned)T;
+              const uint64_t w = anc_s[node[rb] * kMaxAncWords + (in_tree ? (j >> 6) : 0)];
+              const bool vis = key < P || (in_tree && ((w >> (j & 63)) & 1ull));
+              s[rb][h][i] = vis ? s[rb][h][i] : -INFINITY;
+            }
+        }
+        float mo = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mo = fmaxf(mo, s[rb][h][i]);
+        mo *= scale_log2;
+        if (__any(mo > m_run[rb] + 8.0f)) {
+          float rm = fmaxf(mo, __shfl_xor(mo, 16, 64));
+          rm = fmaxf(rm, __shfl_xor(rm, 32, 64));
+          const float m_new = rm > m_run[rb] + 8.0f ? rm : m_run[rb];
+          const float alpha = m_run[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            acc[rb][db][0] *= alpha; acc[rb][db][1] *= alpha;
+            acc[rb][db][2] *= alpha; acc[rb][db][3] *= alpha;
           }
-          x[kb][i] = vis ? s[kb][i] * scale_log2 : -INFINITY;
-          mt = fmaxf(mt, x[kb][i]);
+          l_run[rb] *= alpha;
+          m_run[rb] = m_new;
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      // lazy max: raised only when the tile max exceeds it by more than 2^8
-      const bool raise = mt > m_run[rb] + 8.0f;
-      if (__any(raise)) {
-        const float m_new = raise ? mt : m_run[rb];
-        const float alpha = m_run[rb] == -INFINITY ? 0.f : exp2f(m_run[rb] - m_new);
+        // m is -inf only while every score of the row so far is hidden
+        const float nm = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+        float x[2][4];
+        float psum = 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          acc[rb][db][0] *= alpha; acc[rb][db][1] *= alpha;
-          acc[rb][db][2] *= alpha; acc[rb][db][3] *= alpha;
-        }
-        l_run[rb] *= alpha;
-        m_run[rb] = m_new;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[h][i] = __builtin_amdgcn_exp2f(fmaf(s[rb][h][i], scale_log2, nm));
+            psum += x[h][i];
+          }
+        l_run[rb] += psum;
+        pb[rb].x = pack_bf16x2(x[0][0], x[0][1]);
+        pb[rb].y = pack_bf16x2(x[0][2], x[0][3]);
+        pb[rb].z = pack_bf16x2(x[1][0], x[1][1]);
+        pb[rb].w = pack_bf16x2(x[1][2], x[1][3]);
       }
-      float psum = 0.f;
+      // lane j of group g4 addresses V[32*ks + 4*g4 + j/4 (+16)][16*db + 4*(j%4) .. +4];
+      // the transposing read returns V[32*ks + 4*g4 + i (+16)][16*db + j], i = 0..3
+      const int vrow = 32 * ks + 4 * g4 + (r16 >> 2);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int db = 0; db < DB; ++db) {
+        const int cb = 32 * db + 8 * (r16 & 3);
+        const int ch = cb >> 4, he = (cb & 15) >> 1;
+        const uint2 lo = lds_read_tr16(vb_ + vrow * D + 8 * (ch ^ (vrow & SWZ)) + he);
+        const uint2 hi = lds_read_tr16(vb_ + (vrow + 16) * D + 8 * (ch ^ ((vrow + 16) & SWZ)) + he);
+        uint4 va;
+        va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[kb][i] = x[kb][i] == -INFINITY ? 0.f : exp2f(x[kb][i] - m_run[rb]);
-          psum += x[kb][i];
-        }
-      l_run[rb] += psum;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 pb;   // P^T slots 8*g4 + j <-> keys 32*ks + 16*(j/4) + 4*g4 + j%4
-        pb.x = pack_bf16x2(x[2 * ks][0], x[2 * ks][1]);
-        pb.y = pack_bf16x2(x[2 * ks][2], x[2 * ks][3]);
-        pb.z = pack_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1]);
-        pb.w = pack_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3]);
-        // lane j of group g4 addresses V[32*ks + 4*g4 + j/4 (+16)][16*db + 4*(j%4) .. +4];
-        // the transposing read returns V[32*ks + 4*g4 + i (+16)][16*db + j], i = 0..3
-        const int vrow = 32 * ks + 4 * g4 + (r16 >> 2);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int cb = 32 * db + 8 * (r16 & 3);
-          const int ch = cb >> 4, he = (cb & 15) >> 1;
-          const uint2 lo = lds_read_tr16(vb_ + vrow * D + 8 * (ch ^ (vrow & SWZ)) + he);
-          const uint2 hi = lds_read_tr16(vb_ + (vrow + 16) * D + 8 * (ch ^ ((vrow + 16) & SWZ)) + he);
-          uint4 va;
-          va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-          acc[rb][db] = mfma16x16x32(va, pb, acc[rb][db]);
-        }
+        for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma16x16x32(va, pb[rb], acc[rb][db]);
       }
     }
   };
 
   __syncthreads();   // anc_s
-  if (t_begin < t_end) {
-    const int tl = t_end - 1;
-    load_tile(t_begin);
-    store_tile(0);
-    load_tile(min(t_begin + 1, tl));
-    __syncthreads();
-    for (int tile = t_begin; tile < t_end; ++tile) {
-      const int buf = (tile - t_begin) & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      compute(tile, buf);
-      __builtin_amdgcn_sched_barrier(0);
-      store_tile(buf ^ 1);                 // tile + 1 (a repeat of the last tile at the end)
-      load_tile(min(tile + 2, tl));
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-    }
+  for (int i = 0; i < nt; ++i) {
+    // tiles issued after tile i so far: min(nt - 1 - i, kNBuf - 2), 2*NI issues each
+    const int ahead = min(nt - 1 - i, kNBuf - 2);
+    if (ahead >= 2) vm_wait<4 * NI>();
+    else if (ahead == 1) vm_wait<2 * NI>();
+    else vm_wait<0>();
+    __syncthreads();   // tile i complete from every wave; tile i-1's buffer is free
+    if (i + kNBuf - 1 < nt) issue(t_begin + i + kNBuf - 1, (i + kNBuf - 1) % kNBuf);
+    if (nvb > 0) compute(t_begin + i, i % kNBuf);
   }
 
   // epilogue
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     float l = l_run[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int row = wrow0 + 16 * rb + r16;
+    const int row = blk[rb] * 16 + r16;
     if (row >= rows) continue;
     if (nsplit == 1) {
       const int t = row / G, hg = row - t * G;
@@ -405,23 +448,34 @@ __global__ __launch_bounds__(256) void tree_attn_f32(const float* __restrict__ Q
 }
 
 // ---------------------------------------------------------------- host side
+// Row blocks per wave: enough for all query rows of a kv head in one group
+// when they fit (up to 3 blocks, 384 rows).  Key partitions: one workgroup
+// fits a CU (the LDS ring), so the plan minimises (rounds of 256 workgroups)
+// x (tiles per partition), plus a small charge per partition for the merge.
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
-  AttnPlan p{1, 1, 1, 0};
+  AttnPlan p{1, 1, 1, 0, 1};
   if (dtype != kBF16) return p;
   const int G = nq / nkv;
   const int rows = T * G;
-  p.rb = kRB;
-  p.rowgroups = (rows + kRowsWG - 1) / kRowsWG;
+  p.rb = rows <= 16 * kWaves ? 1 : rows <= 32 * kWaves ? 2 : 3;
+  const int rows_wg = 16 * kWaves * p.rb;
+  p.rowgroups = (rows + rows_wg - 1) / rows_wg;
   const int tiles = (Pmax + kKT2 - 1) / kKT2;
-  const int base = b * nkv * p.rowgroups;
-  // aim at >= 512 workgroups, >= 4 tiles (256 keys) per partition
-  int want = (512 + base - 1) / base;
-  int maxsplit = tiles / 2 > 0 ? tiles / 2 : 1;
-  p.nsplit = want < maxsplit ? want : maxsplit;
-  if (p.nsplit > kMaxSplit) p.nsplit = kMaxSplit;
-  if (p.nsplit < 1) p.nsplit = 1;
+  const long base = (long)b * nkv * p.rowgroups;
+  long best = -1;
+  for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
+    const int tps = (tiles + want - 1) / want;
+    const int ns = (tiles + tps - 1) / tps;
+    const long rounds = (base * ns + 255) / 256;
+    const long cost = 2 * (rounds * tps) + (ns > 1 ? 4 + ns : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      p.nsplit = ns;
+      p.tiles_per_split = tps;
+    }
+  }
   if (p.nsplit > 1) {
-    const size_t rows_pad = (size_t)p.rowgroups * kRowsWG;
+    const size_t rows_pad = (size_t)p.rowgroups * rows_wg;
     p.ws_bytes = (size_t)b * nkv * p.nsplit * rows_pad * ((size_t)d * sizeof(float) + sizeof(float2));
   }
   return p;
@@ -439,10 +493,8 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
     return hipGetLastError();
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  const int tiles = (Pmax + kKT2 - 1) / kKT2;
-  const int tps = (tiles + p.nsplit - 1) / p.nsplit;
   const int rows = T * (nq / nkv);
-  const int rows_pad = p.rowgroups * kRowsWG;
+  const int rows_pad = p.rowgroups * 16 * kWaves * p.rb;
   float* ws_o = static_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + (size_t)b * nkv * p.nsplit * rows_pad * d * sizeof(float));
@@ -451,14 +503,20 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
   const uint16_t* k = static_cast<const uint16_t*>(Kc);
   const uint16_t* v = static_cast<const uint16_t*>(Vc);
   uint16_t* o = static_cast<uint16_t*>(O);
-  if (d == 128)
-    hipLaunchKernelGGL(tree_attn_bf16<128>, dim3(nblk), dim3(kThreads), 0, st, q, k, v, seq_len, anc,
-                       anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit, p.rowgroups, tps, o, ws_o,
-                       ws_ml);
-  else
-    hipLaunchKernelGGL(tree_attn_bf16<64>, dim3(nblk), dim3(kThreads), 0, st, q, k, v, seq_len, anc,
-                       anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit, p.rowgroups, tps, o, ws_o,
-                       ws_ml);
+#define ATTN(D_, RB_)                                                                           \
+  hipLaunchKernelGGL((tree_attn_bf16<D_, RB_>), dim3(nblk), dim3(kThreads), 0, st, q, k, v,     \
+                     seq_len, anc, anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit,            \
+                     p.rowgroups, p.tiles_per_split, o, ws_o, ws_ml)
+  if (d == 128) {
+    if (p.rb == 1) ATTN(128, 1);
+    else if (p.rb == 2) ATTN(128, 2);
+    else ATTN(128, 3);
+  } else {
+    if (p.rb == 1) ATTN(64, 1);
+    else if (p.rb == 2) ATTN(64, 2);
+    else ATTN(64, 3);
+  }
+#undef ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   if (d == 128)

@@ -56,6 +56,7 @@ struct AttnPlan {
   int rowgroups;     // workgroups along the query rows of one kv head
   int rb;            // 16-row blocks per wave
   size_t ws_bytes;
+  int tiles_per_split;  // 64-key tiles per partition
 };
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
 hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const int* seq_len,
