@@ -31,6 +31,8 @@
 // f32 kernel (tiny fp32 workload): one workgroup per (sequence, node, q head),
 // scores staged in LDS, exact two-pass softmax.
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   //   log2 units); only when some lane exceeds m + 8 are the row maxima formed
   //   across the 4 lanes of a row and m raised (O^T and l rescaled), so the
   //   common path has no cross-lane traffic.  p = 2^(s*scale - m) <= 2^8.
-  auto compute = [&](int tile, int buf) {
+  auto compute = [&](int tile, int buf, auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;   // row blocks of this wave with real rows
     const int key0 = tile * kKT2;
     const bool masked = key0 + kKT2 > P;   // uniform: tile reaches the tree slots
     const uint16_t* kb_ = kbuf[buf];
@@ -215,18 +218,18 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < NV; ++rb) s[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int krow = 32 * ks + 16 * h + r16;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
           const uint4 kf = *reinterpret_cast<const uint4*>(kb_ + krow * D + 8 * ((4 * ds + g4) ^ (krow & SWZ)));
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][h] = mfma16x16x32(kf, qf[rb][ds], s[rb][h]);
+          for (int rb = 0; rb < NV; ++rb) s[rb][h] = mfma16x16x32(kf, qf[rb][ds], s[rb][h]);
         }
       }
-      uint4 pb[RB];   // P^T slots 8*g4 + j <-> keys 32*ks + 16*(j/4) + 4*g4 + j%4
+      uint4 pb[NV];   // P^T slots 8*g4 + j <-> keys 32*ks + 16*(j/4) + 4*g4 + j%4
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < NV; ++rb) {
         if (masked) {   // hidden scores become -inf, whose 2^x is 0
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -288,22 +291,30 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
         uint4 va;
         va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma16x16x32(va, pb[rb], acc[rb][db]);
+        for (int rb = 0; rb < NV; ++rb) acc[rb][db] = mfma16x16x32(va, pb[rb], acc[rb][db]);
       }
     }
   };
 
+  // Waves whose last row blocks are empty skip them (MFMA work follows the
+  // real rows); the tile loop is instantiated once per block count.
+  auto run_tiles = [&](auto nv_tag) {
+    for (int i = 0; i < nt; ++i) {
+      // tiles issued after tile i so far: min(nt - 1 - i, kNBuf - 2), 2*NI issues each
+      const int ahead = min(nt - 1 - i, kNBuf - 2);
+      if (ahead >= 2) vm_wait<4 * NI>();
+      else if (ahead == 1) vm_wait<2 * NI>();
+      else vm_wait<0>();
+      __syncthreads();   // tile i complete from every wave; tile i-1's buffer is free
+      if (i + kNBuf - 1 < nt) issue(t_begin + i + kNBuf - 1, (i + kNBuf - 1) % kNBuf);
+      if constexpr (decltype(nv_tag)::value > 0) compute(t_begin + i, i % kNBuf, nv_tag);
+    }
+  };
   __syncthreads();   // anc_s
-  for (int i = 0; i < nt; ++i) {
-    // tiles issued after tile i so far: min(nt - 1 - i, kNBuf - 2), 2*NI issues each
-    const int ahead = min(nt - 1 - i, kNBuf - 2);
-    if (ahead >= 2) vm_wait<4 * NI>();
-    else if (ahead == 1) vm_wait<2 * NI>();
-    else vm_wait<0>();
-    __syncthreads();   // tile i complete from every wave; tile i-1's buffer is free
-    if (i + kNBuf - 1 < nt) issue(t_begin + i + kNBuf - 1, (i + kNBuf - 1) % kNBuf);
-    if (nvb > 0) compute(t_begin + i, i % kNBuf);
-  }
+  if (nvb == RB) run_tiles(std::integral_constant<int, RB>{});
+  else if (RB > 1 && nvb == RB - 1) run_tiles(std::integral_constant<int, RB - 1>{});
+  else if (RB > 2 && nvb == 1) run_tiles(std::integral_constant<int, 1>{});
+  else run_tiles(std::integral_constant<int, 0>{});
 
   // epilogue
 #pragma unroll
