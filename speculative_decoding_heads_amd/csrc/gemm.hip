@@ -15,17 +15,21 @@
 // are the MFMA "A" rows, X rows the "B" columns, so each lane ends up with 4
 // consecutive n of one output row (one 16-byte store of logits).
 //
-// Two bf16 kernels:
-//   gemm_skinny : M <= 8.  HBM-bound weight stream.  A workgroup owns 16*NB
-//                 weight rows; its 4 waves split K and reduce through LDS.
-//                 Both operands go global -> registers (X is tiny and stays in
-//                 L2); each lane loads 64 contiguous bytes per row per step.
-//   gemm_tiled  : 8 < M <= 80 (and heads with larger M).  A workgroup of 8
-//                 waves owns BM = 16*MB activation rows (staged in LDS once per
-//                 K chunk and shared by all waves: re-reading X per wave from
-//                 L2 costs more than the weights) and 128*NBW weight rows (16*NBW
-//                 per wave, direct loads).  Tiles are mapped to XCDs so that the
-//                 M-tiles of one weight tile run on one XCD (L2 reuse).
+// Three bf16 kernels:
+//   gemm_skinny : M <= 16 with fewer than 30720 weight rows.  HBM-bound weight
+//                 stream.  A workgroup owns 16*NB weight rows; its 4 waves
+//                 split K and reduce through LDS.  Both operands go global ->
+//                 registers (X is tiny and stays in L2); each lane loads 64
+//                 contiguous bytes per row per step.
+//   gemm_tiled  : the other M <= 80 cases (and heads with larger M).  A
+//                 workgroup of 8 waves (4 when there are too few weight rows to
+//                 give every CU a 128-row tile) owns BM = 16*MB activation rows
+//                 (staged in LDS once per K chunk and shared by all waves:
+//                 re-reading X per wave from L2 costs more than the weights) and
+//                 16*NBW weight rows per wave (direct loads).  Each workgroup
+//                 starts its K walk at its own chunk, so the workgroups do not
+//                 all read the same slice of X at once.  Tiles are mapped to
+//                 XCDs so that the M-tiles of one weight tile run on one XCD.
 //   gemm_big    : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
@@ -260,9 +264,14 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Each workgroup walks the K chunks from its own starting chunk: every
+  // workgroup reads the same activation rows, and in lockstep they would all
+  // hit the same few L2 channels at once.
+  const int rot = (int)(blockIdx.x % (unsigned)nchunks);
+  auto rc = [&](int c) { const int q = c + rot; return q >= nchunks ? q - nchunks : q; };
   uint4 wa[NBW][4], wb[NBW][4], xr[XP];
   auto loadW = [&](int c, uint4 (&w)[NBW][4]) {
-    const int k0 = c << 7;
+    const int k0 = rc(c) << 7;
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
   };
   auto loadX = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < XP; ++i) xr[i] = ldg16(xsrc[i] + (c << 7));
+    for (int i = 0; i < XP; ++i) xr[i] = ldg16(xsrc[i] + (rc(c) << 7));
   };
   auto storeX = [&](int buf) {
 #pragma unroll
@@ -470,18 +479,28 @@ template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
                               int Kd, const Epi& epi, hipStream_t st) {
   const int mb = (M + 15) / 16;
-  if (M <= 8 || (!std::is_same<Epi, EpiLogits>::value && M <= 16)) {
+  // 8-wave tiled workgroups own 128 weight rows: with enough rows to give
+  // every CU one, they stream best; otherwise skinny (up to 16 rows) or
+  // 4-wave tiled workgroups keep more of them in flight.
+  const bool wide = N >= 240 * 128;
+  if (!wide && M <= 16) {
     // skinny: 4 waves split K, X (a few rows) read from L2
     hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3((N + 31) / 32), dim3(256), 0, st, X, ldx,
                        M, W, N, Kd, epi);
     return hipGetLastError();
   }
-#define TILED(MB_, NBW_)                                                                        \
-  do {                                                                                          \
-    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                            \
-    const int ntn = (N + 128 * NBW_ - 1) / (128 * NBW_);                                        \
-    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 8>), dim3(ntm * ntn), dim3(512), 0, st, \
-                       X, ldx, M, W, N, Kd, ntm, epi);                                          \
+#define TILED(MB_, NBW_)                                                                         \
+  do {                                                                                           \
+    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                             \
+    if (wide) {                                                                                  \
+      const int ntn = (N + 128 * NBW_ - 1) / (128 * NBW_);                                       \
+      hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 8>), dim3(ntm * ntn), dim3(512), 0, st, \
+                         X, ldx, M, W, N, Kd, ntm, epi);                                         \
+    } else {                                                                                     \
+      const int ntn = (N + 64 * NBW_ - 1) / (64 * NBW_);                                         \
+      hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 4>), dim3(ntm * ntn), dim3(256), 0, st, \
+                         X, ldx, M, W, N, Kd, ntm, epi);                                         \
+    }                                                                                            \
   } while (0)
   if constexpr (std::is_same<Epi, EpiLogits>::value) if (mb > 5 && (Kd % 64) == 0) {
     // MFMA-bound: 256 weight rows x 224 or 256 activation rows per workgroup,

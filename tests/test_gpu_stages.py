@@ -32,9 +32,10 @@ HEAD_CASES = [
     # b, H, V, K, dtype
     (1, 128, 1000, 4, "bf16"),     # skinny, one 16-row block, ragged vocab tile
     (3, 256, 4093, 2, "bf16"),     # V % 4 != 0: scalar logit stores
-    (17, 384, 2048, 1, "bf16"),    # 3 K-chunks over 4 waves, 34 rows
-    (16, 256, 3000, 4, "bf16"),    # 80 rows: widest skinny variant
+    (17, 384, 2048, 1, "bf16"),    # 3 K-chunks (odd), 34 rows: 4-wave tiled
+    (16, 256, 3000, 4, "bf16"),    # 80 rows
     (40, 256, 1000, 4, "bf16"),    # 200 rows: tiled kernel, ragged M and N tiles
+    (3, 2048, 1000, 16, "bf16"),   # 32768 head rows: 8-wave tiled, rotated K walk
     (1, 256, 4096, 3, "f32"),      # tiny fp32 workload shape
     (5, 100, 777, 2, "f32"),
 ]
@@ -82,7 +83,9 @@ def test_zero_head_weights_reduce_to_base_head_bitwise(dt):
 
 
 @pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 2000), (11, 256, 4096),
-                                       (2080, 384, 1000), (300, 128, 777), (97, 512, 300)])
+                                       (2080, 384, 1000), (300, 128, 777), (97, 512, 300),
+                                       (5, 384, 31000), (65, 256, 30977), (16, 640, 33000),
+                                       (80, 128, 30720)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
