@@ -26,23 +26,25 @@ __device__ __forceinline__ int row_k(const TopkArgs& a, int i) {
 }
 
 // One workgroup (1024 threads) per row, threshold selection:
-//   A. lanes stream their slice of the row (16-byte loads, a group issued
-//      before use), form the 64-bit keys and keep them in registers (rows up
-//      to 32768 entries; longer rows are re-read from L2 in step C) with the
-//      lane's largest key;
-//   B. tau = the k-th largest of the 1024 lane maxima: each wave takes its k
-//      largest lane maxima (k rounds of a wave max below the previous pick,
-//      shuffle butterflies, no barrier), wave 0 takes the k-th largest of the
-//      16 x k results.  The k largest lane maxima are k distinct entries, so
-//      the row's k-th largest key is >= tau: every top-k entry has key >= tau;
-//   C. lanes append their keys >= tau to an LDS candidate list (about k
+//   A. lanes stream their slice of the row (16-byte loads issued before use;
+//      rows up to 32768 entries stay in registers, longer rows are re-read
+//      from L2 in step C) and keep their largest value with its lowest index;
+//   B. each wave reduces its lanes' (value, index) keys to the wave maximum;
+//      tau = the k-th largest of the 16 wave maxima.  Those k wave maxima are
+//      k distinct entries of the row, so the row's k-th largest key is >= tau
+//      and every top-k entry has key >= tau.  (With fewer than k non-empty
+//      waves tau is 0 and every entry is a candidate.)
+//   C. lanes append the keys >= tau of their entries to an LDS candidate list
+//      (a float compare against tau's value filters first; about k to 3k
 //      entries for continuous data);
-//   D. wave 0 takes the k largest candidates, in order.
-// If ties make the candidate list overflow its LDS capacity, step D instead
-// runs k rounds of "largest key below the previous pick" over the whole row.
+//   D. each candidate's rank is the number of larger candidates (keys are
+//      distinct), and candidates of rank < k write output slot rank.
+// If ties make the candidate list overflow its LDS capacity (or it is long),
+// step D instead runs k rounds of "largest key below the previous pick".
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkKPT = 32;          // keys kept per lane (rows up to 32768 entries)
+constexpr int kTopkKPT = 32;          // entries kept per lane (rows up to 32768 entries)
 constexpr int kTopkCand = 2048;       // LDS candidate capacity
+constexpr int kTopkRankMax = 1024;    // rank selection for up to this many candidates
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -61,13 +63,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
                                                           TopkArgs a, int* __restrict__ root,
                                                           int* __restrict__ idx,
                                                           float* __restrict__ val) {
+  constexpr int NW = kTopkThreads / 64;
   const int row = blockIdx.x;                 // s*(K+1) + i
   const int s = row / (a.K + 1), i = row % (a.K + 1);
   const int k = row_k(a, i);
-  const int tid = threadIdx.x, lane = tid & 63;
-  __shared__ uint64_t red[kTopkThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint64_t red[NW];
   __shared__ uint64_t cand[kTopkCand];
   __shared__ int ncand;
+  __shared__ uint64_t tau_s;
   if (i > 0) {
     for (int r = k + tid; r < a.kmax; r += kTopkThreads) {
       const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
@@ -76,15 +80,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
     }
   }
   if (k == 0) return;
+  if (tid == 0) ncand = 0;
   const float* x = logits + (int64_t)row * a.V;
-  const bool in_regs = (a.V & 3) == 0 && a.V <= kTopkKPT * kTopkThreads;
+  const bool vec = (a.V & 3) == 0;
+  const bool in_regs = vec && a.V <= kTopkKPT * kTopkThreads;
+  const int nv = a.V >> 2;
 
-  // ---- A: keys (in registers when the row fits) and the lane maximum
-  uint64_t keys[kTopkKPT];
-  uint64_t lmax = 0;
+  // ---- A: the lane's largest value, lowest index among equals (entries in
+  // index order: 16-byte group u*1024 + tid, then its 4 entries)
+  f32x4 v[kTopkKPT / 4];
+  float lv = -INFINITY;
+  int li = -1;
   if (in_regs) {
-    const int nv = a.V >> 2;
-    f32x4 v[kTopkKPT / 4];
 #pragma unroll
     for (int u = 0; u < kTopkKPT / 4; ++u) {
       const int e = u * kTopkThreads + tid;
@@ -95,89 +102,122 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       const int e = u * kTopkThreads + tid;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint64_t kk = e < nv ? make_key(v[u][q], 4 * e + q) : 0ull;
-        keys[4 * u + q] = kk;
-        lmax = kk > lmax ? kk : lmax;
+        const bool take = e < nv && (li < 0 || v[u][q] > lv);
+        lv = take ? v[u][q] : lv;
+        li = take ? 4 * e + q : li;
+      }
+    }
+  } else if (vec) {
+    for (int e0 = tid; e0 < nv; e0 += 4 * kTopkThreads) {
+      f32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kTopkThreads;
+        w[u] = e < nv ? *reinterpret_cast<const f32x4*>(x + 4 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kTopkThreads;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool take = e < nv && (li < 0 || w[u][q] > lv);
+          lv = take ? w[u][q] : lv;
+          li = take ? 4 * e + q : li;
+        }
       }
     }
   } else {
     for (int e = tid; e < a.V; e += kTopkThreads) {
-      const uint64_t kk = make_key(x[e], e);
-      lmax = kk > lmax ? kk : lmax;
+      const float y = x[e];
+      const bool take = li < 0 || y > lv;
+      lv = take ? y : lv;
+      li = take ? e : li;
     }
   }
-  // ---- B: tau = k-th largest lane maximum: each wave finds its k largest
-  // lane maxima (wave-local rounds), wave 0 takes the k-th largest of those
-  __shared__ uint64_t wtop[kTopkThreads / 64][kMaxK];
-  __shared__ uint64_t tau_s;
-  {
-    const int wave = tid >> 6;
-    uint64_t p = ~0ull;
-    for (int r = 0; r < k; ++r) {
-      const uint64_t b_ = wave_max_u64(lmax < p ? lmax : 0ull);
-      p = b_;
-      if (lane == 0) wtop[wave][r] = b_;
-    }
-  }
+
+  // ---- B: tau = k-th largest wave maximum
+  const uint64_t wm = wave_max_u64(li >= 0 ? make_key(lv, (uint32_t)li) : 0ull);
+  if (lane == 0) red[wave] = wm;
   __syncthreads();
-  if (tid < 64) {
-    constexpr int NW = kTopkThreads / 64;
-    uint64_t p = ~0ull;
-    for (int r = 0; r < k; ++r) {
-      uint64_t b_ = 0;
-      for (int j = lane; j < NW * k; j += 64) {
-        const uint64_t v = wtop[j / k][j % k];
-        if (v < p && v > b_) b_ = v;
-      }
-      p = wave_max_u64(b_);
+  if (tid < NW) {
+    const uint64_t mine = red[tid];
+    int rank = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rank += red[w] > mine ? 1 : 0;
+    // nonzero keys are distinct: exactly one wave maximum has rank k-1 when at
+    // least k waves hold entries; otherwise tau = 0 (every entry a candidate)
+    if (rank == k - 1 && mine != 0) tau_s = mine;
+    if (tid == 0) {
+      int nz = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) nz += red[w] != 0 ? 1 : 0;
+      if (nz < k) tau_s = 0;
     }
-    if (lane == 0) tau_s = p;
   }
   __syncthreads();
   const uint64_t tau = tau_s;
-  // ---- C: candidates >= tau
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-  if (in_regs) {
-#pragma unroll
-    for (int j = 0; j < kTopkKPT; ++j) {
-      if (keys[j] >= tau && keys[j] != 0) {
-        const int slot = atomicAdd(&ncand, 1);
-        if (slot < kTopkCand) cand[slot] = keys[j];
-      }
-    }
-  } else {
-    for (int e = tid; e < a.V; e += kTopkThreads) {
-      const uint64_t kk = make_key(x[e], e);
+  const float tv = tau ? key_value(tau) : -INFINITY;
+
+  // ---- C: candidates (key >= tau implies value >= tau's value)
+  auto offer = [&](float y, int e) {
+    if (y >= tv) {
+      const uint64_t kk = make_key(y, (uint32_t)e);
       if (kk >= tau) {
         const int slot = atomicAdd(&ncand, 1);
         if (slot < kTopkCand) cand[slot] = kk;
       }
     }
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kTopkKPT / 4; ++u) {
+      const int e = u * kTopkThreads + tid;
+      if (e < nv) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) offer(v[u][q], 4 * e + q);
+      }
+    }
+  } else if (vec) {
+    for (int e = tid; e < nv; e += kTopkThreads) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(x + 4 * e);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) offer(w[q], 4 * e + q);
+    }
+  } else {
+    for (int e = tid; e < a.V; e += kTopkThreads) offer(x[e], e);
   }
   __syncthreads();
   const int nc = ncand;
-  // ---- D: the k largest candidates in order
-  if (nc <= kTopkCand) {
-    if (threadIdx.x < 64) {
+
+  auto emit = [&](int r, uint64_t key) {
+    if (i == 0) {
+      root[s] = (int)key_index(key);
+    } else {
+      const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
+      idx[o] = (int)key_index(key);
+      val[o] = key_value(key);
+    }
+  };
+  // ---- D: rank of each candidate among the candidates
+  if (nc <= kTopkRankMax) {
+    if (tid < nc) {
+      const uint64_t mine = cand[tid];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += cand[j] > mine ? 1 : 0;
+      if (rank < k) emit(rank, mine);
+    }
+  } else if (nc <= kTopkCand) {
+    if (tid < 64) {
       uint64_t p = ~0ull;
       for (int r = 0; r < k; ++r) {
         uint64_t best = 0;
         for (int j = lane; j < nc; j += 64) {
-          const uint64_t v = cand[j];
-          if (v < p && v > best) best = v;
+          const uint64_t c = cand[j];
+          if (c < p && c > best) best = c;
         }
         best = wave_max_u64(best);
         p = best;
-        if (lane == 0) {
-          if (i == 0) {
-            root[s] = (int)key_index(best);
-          } else {
-            const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
-            idx[o] = (int)key_index(best);
-            val[o] = key_value(best);
-          }
-        }
+        if (lane == 0) emit(r, best);
       }
     }
   } else {
@@ -187,25 +227,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       uint64_t best = 0;
       if (in_regs) {
 #pragma unroll
-        for (int j = 0; j < kTopkKPT; ++j)
-          if (keys[j] < p && keys[j] > best) best = keys[j];
+        for (int u = 0; u < kTopkKPT / 4; ++u) {
+          const int e = u * kTopkThreads + tid;
+          if (e < nv) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint64_t kk = make_key(v[u][q], (uint32_t)(4 * e + q));
+              if (kk < p && kk > best) best = kk;
+            }
+          }
+        }
       } else {
         for (int e = tid; e < a.V; e += kTopkThreads) {
-          const uint64_t kk = make_key(x[e], e);
+          const uint64_t kk = make_key(x[e], (uint32_t)e);
           if (kk < p && kk > best) best = kk;
         }
       }
       best = block_max_u64(best, red);
       p = best;
-      if (tid == 0) {
-        if (i == 0) {
-          root[s] = (int)key_index(best);
-        } else {
-          const int64_t o = ((int64_t)s * a.K + (i - 1)) * a.kmax + r;
-          idx[o] = (int)key_index(best);
-          val[o] = key_value(best);
-        }
-      }
+      if (tid == 0) emit(r, best);
     }
   }
 }
