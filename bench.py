@@ -3,7 +3,8 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 heads + LM projection, shortlists, tree, tree attention, verify logits,
-acceptance, KV compaction (seven library calls, see speculative_decoding_heads_amd/step.py).
+acceptance, KV compaction (five library calls: shortlists + tree and acceptance
++ compaction each run as one fused call, see speculative_decoding_heads_amd/step.py).
 Default workload: the Llama-7B shape at batch 1 (hidden 4096, vocab 32000,
 4 heads, 64-candidate tree, 32 heads x 128, prefix 2048, bf16, greedy); the
 batch-16 typical-acceptance variant is measured too and reported alongside.
@@ -36,7 +37,7 @@ METRIC = "Medusa verify steps/sec at 7B shape (bs1, bs16) + % of HBM/MFMA roofli
 PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-CALLS = ["draft_heads", "topk", "build_tree", "tree_attn", "verify_lm", "accept", "kv_compact"]
+CALLS = ["draft_heads", "topk_tree", "tree_attn", "verify_lm", "accept_compact"]
 
 
 def alg_bytes(c):
@@ -47,12 +48,10 @@ def alg_bytes(c):
     return {
         "draft_heads": c.K * c.H * c.H * e + c.V * c.H * e + c.b * c.H * e
         + 2 * rows_d * c.H * e + rows_d * c.V * 4,
-        "topk": rows_d * c.V * 4,
-        "build_tree": c.b * c.T * 8 + c.b * c.K * c.kmax * 4,
+        "topk_tree": rows_d * c.V * 4 + c.b * c.T * 8,
         "tree_attn": 2 * c.b * c.nkv * (c.P + c.T) * c.d * e + 2 * c.b * c.T * c.nq * c.d * e,
         "verify_lm": c.V * c.H * e + rows_v * c.H * e + rows_v * c.V * 4,
-        "accept": rows_v * c.V * 4,
-        "kv_compact": 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
+        "accept_compact": rows_v * c.V * 4 + 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
     }
 
 
@@ -65,30 +64,26 @@ def alg_flops(c):
 
 
 def _enqueue(st, x, step, M, c, ev=None):
-    """The seven calls of VerifyStep.run, with optional events between them."""
+    """The five calls of VerifyStep.run (fused path), with optional events between them."""
     def mark(i):
         if ev is not None:
             ev[i].record()
     mark(0)
     M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
     mark(1)
-    M.medusa_topk(st.logits, c.k, c.kmax, st.mode, c.temperature, c.seed, step, st.root, st.idx,
-                  st.val, st.ws_topk)
+    M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
+                       st.mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx, st.val,
+                       st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
     mark(2)
-    M.medusa_build_tree(c.k, c.N, c.decay.numerator, c.decay.denominator, st.root, st.idx,
-                        x["seq_len"], st.tokens, st.pos, st.parent, st.depth, st.anc)
-    mark(3)
     M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
-    mark(4)
+    mark(3)
     M.medusa_heads(st.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
                    st.base_logits.view(c.b * c.T, c.V), include_base=1)
+    mark(4)
+    M.medusa_accept_compact(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode,
+                            c.temperature, c.eps, c.delta, c.seed, step, st.L, st.path,
+                            st.acc_tokens, st.bonus, x["Kc"], x["Vc"], x["seq_len"], st.ws_acc)
     mark(5)
-    M.medusa_accept(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode, c.temperature,
-                    c.eps, c.delta, c.seed, step, st.L, st.path, st.acc_tokens, st.bonus,
-                    st.ws_acc)
-    mark(6)
-    M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], st.path, st.L)
-    mark(7)
 
 
 def measure(cfg, steps, warmup, rotate=None, log=print):
@@ -132,7 +127,8 @@ def measure(cfg, steps, warmup, rotate=None, log=print):
     ms = start.elapsed_time(end) / steps
 
     # per-call pass
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
+           for _ in range(steps)]
     for j in range(steps):
         i = warmup + steps + j
         _enqueue(st, inputs(i), i, M, c, evs[j])

@@ -148,6 +148,22 @@ int medusa_build_tree(const int32_t* k_host, int32_t K, int32_t N, int32_t decay
                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * medusa_topk_tree - medusa_topk and medusa_build_tree in one launch (the
+ * shortlist of head i and the tokens of the tree nodes at depth i come from
+ * the same workgroup).  Same arguments, layouts and outputs as the two calls
+ * made in sequence: the shortlist arguments of medusa_topk, the tree
+ * arguments of medusa_build_tree (the tree uses the same k_host and kmax),
+ * with seq_len [b] device.  Outputs are bit-identical to the two-call path.
+ * Errors: the union of both calls' checks; nothing is launched on error.
+ * ------------------------------------------------------------------------- */
+int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
+                     int32_t kmax, int32_t N, int32_t decay_num, int32_t decay_den,
+                     int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
+                     const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                     int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
+                     int32_t anc_words, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * medusa_tree_attn - one tree-masked attention layer of the verify pass.
  * [glossary] tree attention: all branches share the prefix KV cache and all
  * nodes are scored in one pass; [deep-dive]: a node attends only to its
@@ -213,6 +229,23 @@ int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t
 int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
                       const int32_t* L, int32_t b, int32_t nkv, int32_t Pmax, int32_t d, int32_t K,
                       int32_t dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_accept_compact - medusa_accept followed by medusa_kv_compact, with
+ * the rollback done by the acceptance walk's own workgroup (one launch less).
+ * Arguments: those of medusa_accept, then the cache arguments of
+ * medusa_kv_compact (Kc, Vc [b, nkv, Pmax, d] dtype, seq_len [b] device, in:
+ * P, out: P + L + 1; K is medusa_accept's K).  Outputs are bit-identical to
+ * the two calls in sequence.  Errors: the union of both calls' checks;
+ * nothing is launched on error.
+ * ------------------------------------------------------------------------- */
+int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const int32_t* parent,
+                          const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K,
+                          int32_t mode, float temperature, float eps, float delta, uint64_t seed,
+                          uint64_t step, int32_t* L, int32_t* path, int32_t* acc_tokens,
+                          int32_t* bonus, void* Kc, void* Vc, int32_t* seq_len, int32_t nkv,
+                          int32_t Pmax, int32_t d, int32_t dtype, void* ws, size_t ws_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

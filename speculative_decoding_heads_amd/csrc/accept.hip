@@ -27,6 +27,7 @@
 //   typical mode then runs the shared float64 row sampler on the chosen node.
 
 #include "common.h"
+#include "compact_dev.h"
 #include "kernels.h"
 
 namespace medusa {
@@ -164,9 +165,14 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
                                                    const Stat* __restrict__ stats,
                                                    int* __restrict__ Lout, int* __restrict__ path,
                                                    int* __restrict__ acc_tokens,
-                                                   int* __restrict__ bonus, int* __restrict__ best_out) {
+                                                   int* __restrict__ bonus, int* __restrict__ best_out,
+                                                   uint8_t* __restrict__ Kc, uint8_t* __restrict__ Vc,
+                                                   int* __restrict__ seq_len, int nkv, int Pmax,
+                                                   int row_bytes) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
+  __shared__ int spath[kMaxHeads + 1];
+  const int P = Kc ? seq_len[s] : 0;
   __shared__ unsigned char local[kMaxT];
   __shared__ int sdepth[kMaxT], sparent[kMaxT];
   __shared__ int bestL, bestNode;
@@ -215,12 +221,21 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
     int a = best;
     for (int d = L; d >= 0; --d) {
       path[(int64_t)s * (K + 1) + d] = a;
+      spath[d] = a;
       acc_tokens[(int64_t)s * (K + 1) + d] = tokens[(int64_t)s * T + a];
       a = a > 0 ? sparent[a] : 0;
     }
     if (MODE == kGreedy) bonus[s] = amax[(int64_t)s * T + best];
     best_out[s] = best;
   }
+  if (!Kc) return;
+  // fused rollback of the accepted path's K/V (the same moves as medusa_kv_compact)
+  __syncthreads();
+  const int L = bestL;
+  const bool ok = P >= 0 && L >= 0 && L <= K;
+  if (ok) compact_columns(Kc, Vc, s, P, L, spath, nkv, Pmax, row_bytes);
+  __syncthreads();
+  if (tid == 0 && ok) seq_len[s] = P + L + 1;
 }
 
 size_t accept_workspace(int b, int T) {
@@ -232,25 +247,30 @@ size_t accept_workspace(int b, int T) {
 hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
                       const int* depth, int b, int T, int V, int K, int mode, float temperature,
                       float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
-                      int* acc_tokens, int* bonus, void* ws, hipStream_t st) {
+                      int* acc_tokens, int* bonus, void* ws, hipStream_t st, const KvRollback* kv) {
   const size_t rows = (size_t)b * T;
   Stat* stats = static_cast<Stat*>(ws);
   int* amax = reinterpret_cast<int*>(stats + rows);
   int* best = amax + rows;
   const float inv_temp = 1.0f / temperature;
+  uint8_t* Kc = kv ? static_cast<uint8_t*>(kv->Kc) : nullptr;
+  uint8_t* Vc = kv ? static_cast<uint8_t*>(kv->Vc) : nullptr;
+  int* seq_len = kv ? kv->seq_len : nullptr;
+  const int nkv = kv ? kv->nkv : 0, Pmax = kv ? kv->Pmax : 0;
+  const int row_bytes = kv ? kv->d * (kv->dtype == kBF16 ? 2 : 4) : 0;
   if (mode == kGreedy) {
     hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
                        V, inv_temp, amax, stats);
     hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
                        parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
-                       acc_tokens, bonus, best);
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
                      V, inv_temp, amax, stats);
   hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
                      depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,
-                     best);
+                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,

@@ -203,6 +203,47 @@ int medusa_build_tree(const int32_t* k_host, int32_t K, int32_t N, int32_t decay
                     "build_tree");
 }
 
+// ------------------------------------------------------------------- top-k + tree, one launch
+int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
+                     int32_t kmax, int32_t N, int32_t decay_num, int32_t decay_den,
+                     int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
+                     const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                     int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
+                     int32_t anc_words, void* ws, size_t ws_bytes, void* stream) {
+  if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
+  if (V <= 0) return fail(MEDUSA_ERR_ARG, "V must be positive");
+  if (kmax < 1 || kmax > MEDUSA_MAX_K) return fail(MEDUSA_ERR_ARG, "kmax out of range [1, 16]");
+  if (int s = check_k(k_host, K, kmax)) return s;
+  for (int i = 0; i < K; ++i)
+    if (k_host[i] > V) return fail(MEDUSA_ERR_ARG, "k_i exceeds V");
+  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL)
+    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY or TYPICAL");
+  if (root_mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  std::shared_ptr<const TreePlanHost> p;
+  if (int s = plan_for(k_host, K, N, decay_num, decay_den, &p)) return s;
+  if (anc_words < (p->T + 63) / 64) return fail(MEDUSA_ERR_ARG, "anc_words < ceil(T / 64)");
+  if (b == 0) return MEDUSA_OK;
+  if (!logits || !root || !idx || !val || !seq_len || !tokens || !pos || !parent || !depth || !anc)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if ((int64_t)b * (K + 1) > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (K+1) > 65535");
+  const size_t need = medusa_topk_workspace(b, K, V, kmax);
+  if (need && (!ws || ws_bytes < need)) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
+  TopkArgs a{};
+  a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
+  a.temperature = temperature; a.seed = seed; a.step = step;
+  for (int i = 0; i < K; ++i) a.k[i] = k_host[i];
+  TreeDev t{};
+  t.T = p->T; t.K = K; t.kmax = kmax; t.anc_words = anc_words;
+  for (int i = 0; i < p->T; ++i) {
+    t.parent[i] = (int16_t)p->parent[i];
+    t.depth[i] = (uint8_t)p->depth[i];
+    t.rank[i] = (uint8_t)(p->rank[i] < 0 ? 0 : p->rank[i]);
+  }
+  TreeOut o{seq_len, tokens, pos, parent, depth, anc};
+  return hip_status(run_topk(logits, a, root, idx, val, ws, as_stream(stream), &t, &o), "topk_tree");
+}
+
 // ------------------------------------------------------------------- attention
 static int attn_check(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d, int32_t Pmax,
                       int32_t dtype) {
@@ -282,6 +323,44 @@ int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t
                                delta, seed, step, L, path, acc_tokens, bonus, ws,
                                as_stream(stream)),
                     "accept");
+}
+
+// ------------------------------------------------------------------- acceptance + rollback
+int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const int32_t* parent,
+                          const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K,
+                          int32_t mode, float temperature, float eps, float delta, uint64_t seed,
+                          uint64_t step, int32_t* L, int32_t* path, int32_t* acc_tokens,
+                          int32_t* bonus, void* Kc, void* Vc, int32_t* seq_len, int32_t nkv,
+                          int32_t Pmax, int32_t d, int32_t dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "V must be positive");
+  if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
+  if (mode == MEDUSA_TYPICAL) {
+    if (!(temperature > 0.f && std::isfinite(temperature)))
+      return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+    if (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta)))
+      return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
+  }
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (nkv < 1 || Pmax < 1 || d < 1) return fail(MEDUSA_ERR_ARG, "bad shape");
+  if ((d * elem_size(dtype)) % 16 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d * sizeof(dtype) must be a multiple of 16");
+  if (b == 0) return MEDUSA_OK;
+  if (!base_logits || !tokens || !parent || !depth || !L || !path || !acc_tokens || !bonus)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!Kc || !Vc || !seq_len) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(Kc) || !aligned16(Vc)) return fail(MEDUSA_ERR_ARG, "cache must be 16-byte aligned");
+  if ((int64_t)b * T > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "b * T too large");
+  const size_t need = medusa_accept_workspace(b, T);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
+  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
+  KvRollback kv{Kc, Vc, seq_len, nkv, Pmax, d, dtype};
+  return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,
+                               delta, seed, step, L, path, acc_tokens, bonus, ws,
+                               as_stream(stream), &kv),
+                    "accept_compact");
 }
 
 // ------------------------------------------------------------------- compaction

@@ -29,23 +29,36 @@ struct TopkArgs {
   uint64_t seed, step;
   int k[kMaxHeads];
 };
-size_t topk_workspace(int b, int K, int V, int kmax);
-hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
-                    void* ws, hipStream_t st);
-
-// ---- sampling rows of softmax(x / T) in float64 (topk.hip)
-// Row of sequence s: base + s*seq_stride + (row_sel ? row_sel[s] : 0) * V.
-hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
-                           float temperature, uint64_t seed, uint64_t step, uint64_t draw,
-                           int* out, hipStream_t st);
-
-// ---- tree gather (tree.hip)
+// ---- tree plan on the device, passed by value (tree.hip, topk.hip)
 struct TreeDev {
   int T, K, kmax, anc_words;
   int16_t parent[kMaxT];
   uint8_t depth[kMaxT];
   uint8_t rank[kMaxT];
 };
+// outputs of the tree gather; tokens == nullptr when no tree is built
+struct TreeOut {
+  const int* seq_len;
+  int* tokens;
+  int* pos;
+  int* parent;
+  int* depth;
+  uint64_t* anc;
+};
+
+size_t topk_workspace(int b, int K, int V, int kmax);
+// With tree != nullptr the same launch also writes the tree tables and tokens.
+hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
+                    void* ws, hipStream_t st, const TreeDev* tree = nullptr,
+                    const TreeOut* tree_out = nullptr);
+
+// ---- sampling rows of softmax(x / T) in float64 (topk.hip)
+// Row of sequence s: base + s*seq_stride + (row_sel ? row_sel[s] : 0) * V.
+// The draw goes to out[s] and, if out2 is given, to out2[s * out2_stride].
+hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
+                           float temperature, uint64_t seed, uint64_t step, uint64_t draw,
+                           int* out, hipStream_t st, int* out2 = nullptr, int out2_stride = 0);
+
 hipError_t run_build_tree(const TreeDev& t, const int* root, const int* idx, int b,
                           const int* seq_len, int* tokens, int* pos, int* parent, int* depth,
                           uint64_t* anc, hipStream_t st);
@@ -65,11 +78,19 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
                          hipStream_t st);
 
 // ---- acceptance (accept.hip)
+// KV cache of the rollback fused into the acceptance walk
+struct KvRollback {
+  void* Kc;
+  void* Vc;
+  int* seq_len;
+  int nkv, Pmax, d, dtype;
+};
 size_t accept_workspace(int b, int T);
 hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
                       const int* depth, int b, int T, int V, int K, int mode, float temperature,
                       float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
-                      int* acc_tokens, int* bonus, void* ws, hipStream_t st);
+                      int* acc_tokens, int* bonus, void* ws, hipStream_t st,
+                      const KvRollback* kv = nullptr);
 
 // ---- compaction (compact.hip)
 hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,

@@ -59,10 +59,29 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   return r;
 }
 
+// Tree tables of one sequence (fused with the shortlists, see topk_tree in
+// run_topk): position ids for every node and, from sequence 0, the static
+// parent / depth / ancestor tables.
+__device__ void tree_common(const TreeDev& t, const TreeOut& o, int s) {
+  const int P = o.seq_len[s];
+  for (int j = threadIdx.x; j < t.T; j += blockDim.x) {
+    o.pos[(int64_t)s * t.T + j] = P + t.depth[j];
+    if (s == 0) {
+      o.parent[j] = t.parent[j];
+      o.depth[j] = t.depth[j];
+      uint64_t w[kMaxAncWords] = {0, 0, 0, 0};
+      for (int a = j; a >= 0; a = t.parent[a]) w[a >> 6] |= 1ull << (a & 63);
+      for (int q = 0; q < t.anc_words; ++q)
+        o.anc[(int64_t)j * t.anc_words + q] = q < kMaxAncWords ? w[q] : 0;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restrict__ logits,
                                                           TopkArgs a, int* __restrict__ root,
                                                           int* __restrict__ idx,
-                                                          float* __restrict__ val) {
+                                                          float* __restrict__ val, TreeDev t,
+                                                          TreeOut to) {
   constexpr int NW = kTopkThreads / 64;
   const int row = blockIdx.x;                 // s*(K+1) + i
   const int s = row / (a.K + 1), i = row % (a.K + 1);
@@ -79,7 +98,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       val[o] = -INFINITY;
     }
   }
-  if (k == 0) return;
+  const bool tree = to.tokens != nullptr;
+  if (k == 0) {            // typical root row: drawn by sample_rows
+    if (tree && i == 0) tree_common(t, to, s);
+    return;
+  }
   if (tid == 0) ncand = 0;
   const float* x = logits + (int64_t)row * a.V;
   const bool vec = (a.V & 3) == 0;
@@ -189,7 +212,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
   __syncthreads();
   const int nc = ncand;
 
+  __shared__ int res[kMaxK];
   auto emit = [&](int r, uint64_t key) {
+    res[r] = (int)key_index(key);
     if (i == 0) {
       root[s] = (int)key_index(key);
     } else {
@@ -248,6 +273,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       if (tid == 0) emit(r, best);
     }
   }
+  if (!tree) return;
+  // ---- tree tokens: the nodes whose last rank lies in this head's shortlist
+  __syncthreads();
+  if (i == 0) {
+    tree_common(t, to, s);
+    if (tid == 0) to.tokens[(int64_t)s * t.T] = res[0];
+  } else {
+    for (int j = tid; j < t.T; j += kTopkThreads)
+      if (t.depth[j] == i) to.tokens[(int64_t)s * t.T + j] = res[t.rank[j]];
+  }
 }
 
 size_t topk_workspace(int b, int K, int V, int kmax) {
@@ -256,15 +291,23 @@ size_t topk_workspace(int b, int K, int V, int kmax) {
 }
 
 hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
-                    void* ws, hipStream_t st) {
+                    void* ws, hipStream_t st, const TreeDev* tree, const TreeOut* tree_out) {
   (void)ws;
   const int rows = a.b * (a.K + 1);
-  hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(kTopkThreads), 0, st, logits, a, root, idx, val);
+  TreeDev t{};
+  TreeOut o{};
+  if (tree) {
+    t = *tree;
+    o = *tree_out;
+  }
+  hipLaunchKernelGGL(topk_rows, dim3(rows), dim3(kTopkThreads), 0, st, logits, a, root, idx, val, t,
+                     o);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.root_mode == kTypical)
     return run_sample_rows(logits, (int64_t)(a.K + 1) * a.V, nullptr, a.b, a.V, a.temperature,
-                           a.seed, a.step, 0, root, st);
+                           a.seed, a.step, 0, root, st, tree ? o.tokens : nullptr,
+                           tree ? t.T : 0);
   return hipSuccess;
 }
 
@@ -276,7 +319,9 @@ __global__ __launch_bounds__(kSampThreads) void sample_rows(const float* __restr
                                                             const int* __restrict__ row_sel, int V,
                                                             float temperature, uint64_t seed,
                                                             uint64_t step, uint64_t draw,
-                                                            int* __restrict__ out) {
+                                                            int* __restrict__ out,
+                                                            int* __restrict__ out2,
+                                                            int out2_stride) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NW = kSampThreads / 64;
@@ -336,14 +381,17 @@ __global__ __launch_bounds__(kSampThreads) void sample_rows(const float* __restr
     found = pick;
   }
   __syncthreads();
-  if (tid == 0) out[s] = found;
+  if (tid == 0) {
+    out[s] = found;
+    if (out2) out2[(int64_t)s * out2_stride] = found;
+  }
 }
 
 hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
                            float temperature, uint64_t seed, uint64_t step, uint64_t draw,
-                           int* out, hipStream_t st) {
+                           int* out, hipStream_t st, int* out2, int out2_stride) {
   hipLaunchKernelGGL(sample_rows, dim3(b), dim3(kSampThreads), 0, st, base, seq_stride, row_sel, V,
-                     temperature, seed, step, draw, out);
+                     temperature, seed, step, draw, out, out2, out2_stride);
   return hipGetLastError();
 }
 

@@ -55,6 +55,11 @@ _SIGS = {
     "medusa_accept": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _F, _F, _U64, _U64, _P, _P,
                        _P, _P, _P, _SZ, _P], _I32),
     "medusa_kv_compact": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
+    "medusa_topk_tree": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _F, _U64, _U64,
+                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P], _I32),
+    "medusa_accept_compact": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _F, _F, _U64, _U64,
+                               _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P],
+                              _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -101,6 +106,32 @@ def _i32_host(values):
     return arr
 
 
+def _need(cond, what):
+    """Shape / dtype agreement between the tensors of one call (the C ABI takes
+    raw pointers and sizes, so a mismatch here would become an out-of-bounds
+    access there)."""
+    if not cond:
+        raise ValueError(what)
+
+
+def _shape(t, shape, name):
+    _need(t is not None and tuple(t.shape) == tuple(shape),
+          f"{name}: expected shape {tuple(shape)}, got {None if t is None else tuple(t.shape)}")
+
+
+def _dt(t, dtype, name):
+    _need(t.dtype == dtype, f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _tree_T(k, N, decay_num, decay_den):
+    kk = _i32_host(k)
+    T = ctypes.c_int32(0)
+    st = lib().medusa_tree_plan(kk, len(k), -1 if N is None else N, decay_num, decay_den, None,
+                                None, None, 0, ctypes.byref(T))
+    _check("medusa_tree_plan", st)
+    return T.value
+
+
 def dtype_code(t):
     if t.dtype == torch.bfloat16:
         return BF16
@@ -136,15 +167,53 @@ def medusa_heads(x, W, LM, logits, include_base=1, u_out=None, ws=None, stream=N
     rows, H = x.shape
     n_heads = 0 if W is None else W.shape[0]
     V = LM.shape[0]
+    R = (1 if include_base else 0) + n_heads
+    _shape(LM, (V, H), "LM")
+    _dt(LM, x.dtype, "LM")
+    if W is not None:
+        _shape(W, (n_heads, H, H), "W")
+        _dt(W, x.dtype, "W")
+    _need(logits.numel() == rows * R * V and logits.shape[-1] == V, "logits: expected rows*R*V entries")
+    _dt(logits, torch.float32, "logits")
+    if u_out is not None:
+        _need(u_out.numel() == rows * R * H and u_out.shape[-1] == H, "u_out: expected rows*R*H entries")
+        _dt(u_out, x.dtype, "u_out")
     st = lib().medusa_heads(_ptr(x), rows, H, _ptr(W), n_heads, _ptr(LM), V, dtype_code(x),
                             include_base, _ptr(u_out), _ptr(logits), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream(stream))
     _check("medusa_heads", st)
 
 
+def _topk_shapes(logits, k, kmax, root, idx, val):
+    b, K1, V = logits.shape
+    _dt(logits, torch.float32, "logits")
+    _need(len(k) == K1 - 1, "len(k) must equal the number of head rows K")
+    _shape(root, (b,), "root")
+    _shape(idx, (b, K1 - 1, kmax), "idx")
+    _shape(val, (b, K1 - 1, kmax), "val")
+    _dt(root, torch.int32, "root")
+    _dt(idx, torch.int32, "idx")
+    _dt(val, torch.float32, "val")
+
+
+def _tree_shapes(T, b, seq_len, tokens, pos, parent, depth, anc):
+    _shape(seq_len, (b,), "seq_len")
+    _shape(tokens, (b, T), "tokens")
+    _shape(pos, (b, T), "pos")
+    _shape(parent, (T,), "parent")
+    _shape(depth, (T,), "depth")
+    _need(anc.dim() == 2 and anc.shape[0] == T and anc.shape[1] >= (T + 63) // 64,
+          "anc: expected [T, >= ceil(T/64)]")
+    for t, n in ((seq_len, "seq_len"), (tokens, "tokens"), (pos, "pos"), (parent, "parent"),
+                 (depth, "depth")):
+        _dt(t, torch.int32, n)
+    _dt(anc, torch.int64, "anc")
+
+
 def medusa_topk(logits, k, kmax, root_mode, temperature, seed, step, root, idx, val, ws,
                 stream=None):
     b, K1, V = logits.shape
+    _topk_shapes(logits, k, kmax, root, idx, val)
     st = lib().medusa_topk(_ptr(logits), b, K1 - 1, V, _i32_host(k), kmax, root_mode,
                            temperature, seed, step, _ptr(root), _ptr(idx), _ptr(val), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream(stream))
@@ -169,6 +238,9 @@ def medusa_tree_plan(k, N, decay_num=4, decay_den=5):
 def medusa_build_tree(k, N, decay_num, decay_den, root, idx, seq_len, tokens, pos, parent, depth,
                       anc, stream=None):
     b, K, kmax = idx.shape
+    _need(len(k) == K, "len(k) must equal idx.shape[1]")
+    _shape(root, (b,), "root")
+    _tree_shapes(_tree_T(k, N, decay_num, decay_den), b, seq_len, tokens, pos, parent, depth, anc)
     st = lib().medusa_build_tree(_i32_host(k), len(k), -1 if N is None else N, decay_num,
                                  decay_den, _ptr(root), _ptr(idx), b, kmax, _ptr(seq_len),
                                  _ptr(tokens), _ptr(pos), _ptr(parent), _ptr(depth), _ptr(anc),
@@ -179,6 +251,14 @@ def medusa_build_tree(k, N, decay_num, decay_den, root, idx, seq_len, tokens, po
 def medusa_tree_attn(Q, Kc, Vc, seq_len, anc, O, scale=None, ws=None, stream=None):
     b, T, nq, d = Q.shape
     nkv, Pmax = Kc.shape[1], Kc.shape[2]
+    _shape(Kc, (b, nkv, Pmax, d), "Kc")
+    _shape(Vc, (b, nkv, Pmax, d), "Vc")
+    _shape(seq_len, (b,), "seq_len")
+    _dt(seq_len, torch.int32, "seq_len")
+    _need(anc.dim() == 2 and anc.shape[0] == T, "anc: expected [T, words]")
+    _need(O.numel() == b * T * nq * d, "O: expected b*T*nq*d entries")
+    for t, n in ((Kc, "Kc"), (Vc, "Vc"), (O, "O")):
+        _dt(t, Q.dtype, n)
     if scale is None:
         scale = d ** -0.5
     st = lib().medusa_tree_attn(_ptr(Q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(anc), anc.shape[1],
@@ -187,9 +267,25 @@ def medusa_tree_attn(Q, Kc, Vc, seq_len, anc, O, scale=None, ws=None, stream=Non
     _check("medusa_tree_attn", st)
 
 
+def _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus):
+    b, T, V = base_logits.shape
+    _dt(base_logits, torch.float32, "base_logits")
+    _shape(tokens, (b, T), "tokens")
+    _shape(parent, (T,), "parent")
+    _shape(depth, (T,), "depth")
+    _shape(L, (b,), "L")
+    _shape(path, (b, K + 1), "path")
+    _shape(acc_tokens, (b, K + 1), "acc_tokens")
+    _shape(bonus, (b,), "bonus")
+    for t, n in ((tokens, "tokens"), (parent, "parent"), (depth, "depth"), (L, "L"),
+                 (path, "path"), (acc_tokens, "acc_tokens"), (bonus, "bonus")):
+        _dt(t, torch.int32, n)
+
+
 def medusa_accept(base_logits, tokens, parent, depth, K, mode, temperature, eps, delta, seed, step,
                   L, path, acc_tokens, bonus, ws, stream=None):
     b, T, V = base_logits.shape
+    _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus)
     st = lib().medusa_accept(_ptr(base_logits), _ptr(tokens), _ptr(parent), _ptr(depth), b, T, V, K,
                              mode, temperature, eps, delta, seed, step, _ptr(L), _ptr(path),
                              _ptr(acc_tokens), _ptr(bonus), _ptr(ws),
@@ -197,9 +293,49 @@ def medusa_accept(base_logits, tokens, parent, depth, K, mode, temperature, eps,
     _check("medusa_accept", st)
 
 
+def _cache_shapes(Kc, Vc, seq_len, b):
+    _need(Kc.dim() == 4 and Kc.shape[0] == b, "Kc: expected [b, nkv, Pmax, d]")
+    _shape(Vc, tuple(Kc.shape), "Vc")
+    _dt(Vc, Kc.dtype, "Vc")
+    _shape(seq_len, (b,), "seq_len")
+    _dt(seq_len, torch.int32, "seq_len")
+
+
 def medusa_kv_compact(Kc, Vc, seq_len, path, L, stream=None):
     b, nkv, Pmax, d = Kc.shape
     K = path.shape[1] - 1
+    _cache_shapes(Kc, Vc, seq_len, b)
+    _shape(path, (b, K + 1), "path")
+    _shape(L, (b,), "L")
     st = lib().medusa_kv_compact(_ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(path), _ptr(L), b, nkv,
                                  Pmax, d, K, dtype_code(Kc), _stream(stream))
     _check("medusa_kv_compact", st)
+
+
+def medusa_topk_tree(logits, k, kmax, N, decay_num, decay_den, root_mode, temperature, seed, step,
+                     seq_len, root, idx, val, tokens, pos, parent, depth, anc, ws, stream=None):
+    b, K1, V = logits.shape
+    _topk_shapes(logits, k, kmax, root, idx, val)
+    _tree_shapes(_tree_T(k, N, decay_num, decay_den), b, seq_len, tokens, pos, parent, depth, anc)
+    st = lib().medusa_topk_tree(_ptr(logits), b, K1 - 1, V, _i32_host(k), kmax,
+                                -1 if N is None else N, decay_num, decay_den, root_mode,
+                                temperature, seed, step, _ptr(seq_len), _ptr(root), _ptr(idx),
+                                _ptr(val), _ptr(tokens), _ptr(pos), _ptr(parent), _ptr(depth),
+                                _ptr(anc), anc.shape[1], _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(stream))
+    _check("medusa_topk_tree", st)
+
+
+def medusa_accept_compact(base_logits, tokens, parent, depth, K, mode, temperature, eps, delta,
+                          seed, step, L, path, acc_tokens, bonus, Kc, Vc, seq_len, ws,
+                          stream=None):
+    b, T, V = base_logits.shape
+    _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus)
+    _cache_shapes(Kc, Vc, seq_len, b)
+    _, nkv, Pmax, d = Kc.shape
+    st = lib().medusa_accept_compact(_ptr(base_logits), _ptr(tokens), _ptr(parent), _ptr(depth), b,
+                                     T, V, K, mode, temperature, eps, delta, seed, step, _ptr(L),
+                                     _ptr(path), _ptr(acc_tokens), _ptr(bonus), _ptr(Kc), _ptr(Vc),
+                                     _ptr(seq_len), nkv, Pmax, d, dtype_code(Kc), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream))
+    _check("medusa_accept_compact", st)

@@ -11,6 +11,9 @@ accept and roll back); every part of the step runs in the HIP kernels.
                  medusa_heads(O, base only) -> base_logits [b, T, V]
     accept     : medusa_accept              -> L, path, acc_tokens, bonus
     rollback   : medusa_kv_compact          -> Kc, Vc, seq_len updated
+
+With ``fused=True`` (the default) shortlists + tree run as medusa_topk_tree and
+accept + rollback as medusa_accept_compact: the same outputs, two launches fewer.
 """
 
 import torch
@@ -52,24 +55,36 @@ class VerifyStep:
             M.medusa_tree_attn_workspace(c.b, T, c.nq, c.nkv, c.d, c.Pmax, dt), device)
         self.ws_acc = M.workspace(M.medusa_accept_workspace(c.b, T), device)
 
-    def run(self, x, step=0, stream=None):
+    def run(self, x, step=0, stream=None, fused=True):
         """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len."""
         c = self.cfg
         M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
                        stream=stream)
-        M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step, self.root,
-                      self.idx, self.val, self.ws_topk, stream=stream)
-        M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
-                            self.idx, x["seq_len"], self.tokens, self.pos, self.parent,
-                            self.depth, self.anc, stream=stream)
+        if fused:
+            M.medusa_topk_tree(self.logits, c.k, c.kmax, self.N, c.decay.numerator,
+                               c.decay.denominator, self.mode, c.temperature, c.seed, step,
+                               x["seq_len"], self.root, self.idx, self.val, self.tokens, self.pos,
+                               self.parent, self.depth, self.anc, self.ws_topk, stream=stream)
+        else:
+            M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step,
+                          self.root, self.idx, self.val, self.ws_topk, stream=stream)
+            M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
+                                self.idx, x["seq_len"], self.tokens, self.pos, self.parent,
+                                self.depth, self.anc, stream=stream)
         M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], self.anc, self.O,
                            ws=self.ws_attn, stream=stream)
         M.medusa_heads(self.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
                        self.base_logits.view(c.b * c.T, c.V), include_base=1, stream=stream)
-        M.medusa_accept(self.base_logits, self.tokens, self.parent, self.depth, c.K, self.mode,
-                        c.temperature, c.eps, c.delta, c.seed, step, self.L, self.path,
-                        self.acc_tokens, self.bonus, self.ws_acc, stream=stream)
-        M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], self.path, self.L, stream=stream)
+        if fused:
+            M.medusa_accept_compact(self.base_logits, self.tokens, self.parent, self.depth, c.K,
+                                    self.mode, c.temperature, c.eps, c.delta, c.seed, step, self.L,
+                                    self.path, self.acc_tokens, self.bonus, x["Kc"], x["Vc"],
+                                    x["seq_len"], self.ws_acc, stream=stream)
+        else:
+            M.medusa_accept(self.base_logits, self.tokens, self.parent, self.depth, c.K, self.mode,
+                            c.temperature, c.eps, c.delta, c.seed, step, self.L, self.path,
+                            self.acc_tokens, self.bonus, self.ws_acc, stream=stream)
+            M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], self.path, self.L, stream=stream)
 
 
 def device_inputs(cfg, host, device="cuda"):

@@ -132,3 +132,29 @@ def test_workspace_queries_are_host_only_and_sized():
     # the 7B batch-1 attention splits the prefix; the long-context batch-32 one does not
     assert M.medusa_tree_attn_workspace(1, 65, 32, 32, 128, 2048 + 65, M.BF16) > 0
     assert M.medusa_tree_attn_workspace(1, 11, 4, 4, 64, 139, M.F32) == 0
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks that the tensors of a call agree before it passes raw
+    pointers and sizes to the library (CPU tensors: the check comes first)."""
+    import torch
+    bf = torch.bfloat16
+    x = torch.zeros(2, 128, dtype=bf)
+    with pytest.raises(ValueError, match="LM"):
+        M.medusa_heads(x, None, torch.zeros(100, 256, dtype=bf), torch.zeros(2, 1, 100))
+    with pytest.raises(ValueError, match="W"):
+        M.medusa_heads(x, torch.zeros(3, 128, 64, dtype=bf), torch.zeros(100, 128, dtype=bf),
+                       torch.zeros(2, 4, 100))
+    with pytest.raises(ValueError, match="logits"):
+        M.medusa_heads(x, None, torch.zeros(100, 128, dtype=bf), torch.zeros(2, 1, 99))
+    Q = torch.zeros(1, 5, 2, 64, dtype=bf)
+    Kc = torch.zeros(1, 2, 20, 64, dtype=bf)
+    with pytest.raises(ValueError, match="O"):
+        M.medusa_tree_attn(Q, Kc, Kc.clone(), torch.zeros(1, dtype=torch.int32),
+                           torch.zeros(5, 1, dtype=torch.int64), torch.zeros(1, 5, 64, dtype=bf))
+    i32 = dict(dtype=torch.int32)
+    with pytest.raises(ValueError, match="path"):
+        M.medusa_accept(torch.zeros(1, 5, 10), torch.zeros(1, 5, **i32), torch.zeros(5, **i32),
+                        torch.zeros(5, **i32), 2, M.GREEDY, 1.0, 0.3, 0.09, 0, 0,
+                        torch.zeros(1, **i32), torch.zeros(1, 2, **i32), torch.zeros(1, 3, **i32),
+                        torch.zeros(1, **i32), None)

@@ -1,0 +1,57 @@
+"""The fused calls against the separate ones, bit for bit.
+
+medusa_topk_tree must write exactly what medusa_topk followed by
+medusa_build_tree writes, and medusa_accept_compact exactly what medusa_accept
+followed by medusa_kv_compact writes (outputs, cache and seq_len).  Both paths
+run from identical device inputs; the separate path is itself checked against
+the oracle in test_gpu_stages / test_gpu_fullsize.
+"""
+
+import pytest
+import torch
+
+from speculative_decoding_heads_amd import configs as C
+from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
+from speculative_decoding_heads_amd.synth import make_inputs
+from tests.helpers import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    C.TINY,
+    # bf16, greedy, sparse tree, grouped heads
+    C.Config("fused_bf16_greedy", 91, 3, 256, 3000, (4, 3, 2), 20, 4, 2, 64, 300, "bf16", "greedy"),
+    # bf16, typical (the root and the next token are counter draws), long-ish tree
+    C.Config("fused_bf16_typical", 92, 2, 384, 5000, (5, 4, 3, 2), 60, 6, 3, 64, 700, "bf16",
+             "typical"),
+    C.LLAMA7B_BS1,
+]
+
+OUTS = ("logits", "root", "idx", "val", "tokens", "pos", "parent", "depth", "anc", "O",
+        "base_logits", "L", "path", "acc_tokens", "bonus")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_fused_calls_match_separate_calls(cfg):
+    say("fused vs separate", cfg.name)
+    host = make_inputs(cfg)
+    res = {}
+    for fused in (False, True):
+        x = device_inputs(cfg, host)
+        st = VerifyStep(cfg)
+        st.run(x, step=3, fused=fused)
+        torch.cuda.synchronize()
+        res[fused] = ({k: getattr(st, k).clone() for k in OUTS},
+                      {k: x[k].clone() for k in ("Kc", "Vc", "seq_len")})
+    (a, ca), (b, cb) = res[False], res[True]
+    for k in OUTS:
+        assert torch.equal(a[k], b[k]), k
+    for k in ("Kc", "Vc", "seq_len"):
+        assert torch.equal(ca[k], cb[k]), k
+    # the rollback did run: seq_len = P + L + 1
+    assert torch.equal(cb["seq_len"].cpu(), cfg.P + b["L"].cpu() + 1)
