@@ -9,32 +9,67 @@
 //
 // In-place hazard: slot P + d is written while slot P + path[d'] may still be
 // needed.  Nodes are numbered breadth-first, so path[d'] >= d' for every d';
-// each thread owns a fixed 16-byte column of the (kv head, dim) slab and walks
-// d = 0..L in order, reading slot P + path[d] before writing slot P + d.  A
-// later source path[d'] (d' > d) is never a slot written earlier (path[d'] >= d'
-// > d), and different threads touch disjoint columns, so no barrier is needed
-// between the moves.
+// each thread owns a fixed 16-byte column of the (kv head, dim) slab and moves
+// d = 0..L in order (reads of a group of four before its writes), so a later
+// source path[d'] (d' > d) is never a slot written earlier, and different
+// threads touch disjoint columns: no barrier is needed between the moves.
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace medusa {
 
+// Moves of one sequence; pth[d], d = 0..L <= kMaxHeads, is the accepted path.
+// A thread takes up to four of its columns at a time and moves them in
+// groups of four consecutive d: all sixteen source reads are in flight
+// together before the group's writes.  Safe because path[d'] >= d' > d for
+// every later d', so no later read hits a slot written before it.  Slots out
+// of range (only with an inconsistent seq_len or path) are left alone.
 __device__ __forceinline__ void compact_columns(uint8_t* __restrict__ Kc, uint8_t* __restrict__ Vc,
                                                 int s, int P, int L, const int* pth, int nkv,
                                                 int Pmax, int row_bytes) {
+  constexpr int IB = 4;                           // columns per thread per pass
   const int cols = row_bytes / 16;                // 16-byte columns per kv head row
   const int64_t slab = (int64_t)Pmax * row_bytes;  // bytes per (sequence, kv head)
-  for (int item = threadIdx.x; item < 2 * nkv * cols; item += blockDim.x) {
-    const int which = item / (nkv * cols);
-    const int rem = item - which * nkv * cols;
-    const int g = rem / cols, c = rem - g * cols;
-    uint8_t* base = (which ? Vc : Kc) + ((int64_t)s * nkv + g) * slab + (int64_t)c * 16;
-    for (int d = 0; d <= L; ++d) {
-      const int src = pth[d];
-      if (src == d || src < 0 || P + src >= Pmax || P + d >= Pmax) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)(P + src) * row_bytes);
-      *reinterpret_cast<uint4*>(base + (int64_t)(P + d) * row_bytes) = v;
+  const int nitems = 2 * nkv * cols;
+  for (int i0 = threadIdx.x; i0 < nitems; i0 += IB * blockDim.x) {
+    uint8_t* base[IB];
+    bool live[IB];
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const int item = i0 + j * blockDim.x;
+      live[j] = item < nitems;
+      const int it = live[j] ? item : i0;
+      const int which = it / (nkv * cols);
+      const int rem = it - which * nkv * cols;
+      const int g = rem / cols, c = rem - g * cols;
+      base[j] = (which ? Vc : Kc) + ((int64_t)s * nkv + g) * slab + (int64_t)c * 16;
+    }
+    for (int d0 = 0; d0 <= L; d0 += 4) {
+      int src[4];
+      bool mv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = d0 + q;
+        const int sd = d <= L ? pth[d] : d;
+        mv[q] = !(sd == d || sd < 0 || P + sd >= Pmax || P + d >= Pmax);
+        src[q] = mv[q] ? P + sd : min(P, Pmax - 1);   // otherwise a discarded in-range read
+      }
+      if (!(mv[0] || mv[1] || mv[2] || mv[3])) continue;   // nothing moves in this group
+      typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+      u32x4 v[IB][4];
+#pragma unroll
+      for (int j = 0; j < IB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[j][q] = *reinterpret_cast<const u32x4*>(base[j] + (int64_t)src[q] * row_bytes);
+#pragma unroll
+      for (int j = 0; j < IB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (live[j] && mv[q])
+            *reinterpret_cast<u32x4*>(base[j] + (int64_t)(P + d0 + q) * row_bytes) = v[j][q];
     }
   }
 }

@@ -489,18 +489,26 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
                        M, W, N, Kd, epi);
     return hipGetLastError();
   }
-#define TILED(MB_, NBW_)                                                                         \
-  do {                                                                                           \
-    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                             \
-    if (wide) {                                                                                  \
-      const int ntn = (N + 128 * NBW_ - 1) / (128 * NBW_);                                       \
-      hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 8>), dim3(ntm * ntn), dim3(512), 0, st, \
-                         X, ldx, M, W, N, Kd, ntm, epi);                                         \
-    } else {                                                                                     \
-      const int ntn = (N + 64 * NBW_ - 1) / (64 * NBW_);                                         \
-      hipLaunchKernelGGL((gemm_tiled_bf16<MB_, NBW_, Epi, 4>), dim3(ntm * ntn), dim3(256), 0, st, \
-                         X, ldx, M, W, N, Kd, ntm, epi);                                         \
-    }                                                                                            \
+  // Wide weights: 8-wave workgroups of 128 rows; when that leaves a partial
+  // last round of workgroups on the 256 CUs (N between 2048 and 4096 16-row
+  // blocks), 10/12/16-wave workgroups make exactly one round instead.
+  const int units = (N + 15) / 16;
+  const int nw = units <= 8 * 256 || units > 16 * 256 ? 8
+                 : units <= 10 * 256 ? 10 : units <= 12 * 256 ? 12 : 16;
+#define TILED_NW(MB_, NW_)                                                                     \
+  do {                                                                                         \
+    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
+    const int ntn = (N + 16 * NW_ - 1) / (16 * NW_);                                           \
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * ntn), dim3(64 * NW_), 0, \
+                       st, X, ldx, M, W, N, Kd, ntm, epi);                                     \
+  } while (0)
+#define TILED(MB_, NBW_)                                                                       \
+  do {                                                                                         \
+    if (!wide) TILED_NW(MB_, 4);                                                               \
+    else if (MB_ > 5 || nw == 8) TILED_NW(MB_, 8);                                             \
+    else if (nw == 10) TILED_NW(MB_, (MB_ > 5 ? 8 : 10));                                      \
+    else if (nw == 12) TILED_NW(MB_, (MB_ > 5 ? 8 : 12));                                      \
+    else TILED_NW(MB_, (MB_ > 5 ? 8 : 16));                                                    \
   } while (0)
   if constexpr (std::is_same<Epi, EpiLogits>::value) if (mb > 5 && (Kd % 64) == 0) {
     // MFMA-bound: 256 weight rows x 224 or 256 activation rows per workgroup,
@@ -529,6 +537,7 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     default: TILED(8, 1); break;
   }
 #undef TILED
+#undef TILED_NW
   return hipGetLastError();
 }
 

@@ -85,7 +85,8 @@ def test_zero_head_weights_reduce_to_base_head_bitwise(dt):
 @pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 2000), (11, 256, 4096),
                                        (2080, 384, 1000), (300, 128, 777), (97, 512, 300),
                                        (5, 384, 31000), (65, 256, 30977), (16, 640, 33000),
-                                       (80, 128, 30720)])
+                                       (80, 128, 30720), (5, 256, 40000), (65, 128, 50000),
+                                       (16, 256, 60000)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
@@ -354,6 +355,28 @@ def test_kv_compact_exact(dt, nkv, d):
     paths = np.array([[0, 2, 5, 9, 20], [0, 1, 2, 3, 4], [0, -1, -1, -1, -1], [0, 3, 8, -1, -1]],
                      dtype=np.int32)
     Ls = np.array([4, 4, 0, 2], dtype=np.int32)
+    seq = torch.full((b,), P, dtype=torch.int32, device=DEV)
+    Kd, Vd = Kc.to(DEV), Vc.to(DEV)
+    M.medusa_kv_compact(Kd, Vd, seq, torch.from_numpy(paths).to(DEV), torch.from_numpy(Ls).to(DEV))
+    torch.cuda.synchronize()
+    for s in range(b):
+        Kn, Vn, n = kv_compact(Kc[s].float().numpy(), Vc[s].float().numpy(), P, paths[s], int(Ls[s]))
+        assert int(seq[s]) == n
+        assert np.array_equal(Kd[s].float().cpu().numpy(), Kn)
+        assert np.array_equal(Vd[s].float().cpu().numpy(), Vn)
+
+
+def test_kv_compact_long_paths():
+    """Paths of up to 17 nodes (K = 16): several groups of moves per column."""
+    tdt = torch.bfloat16
+    b, K, nkv, d, P, T = 3, 16, 2, 64, 50, 40
+    Pmax = P + T
+    Kc = normal((b, nkv, Pmax, d), 15, 1.0, tdt)
+    Vc = normal((b, nkv, Pmax, d), 16, 1.0, tdt)
+    full = [0, 1, 3, 4, 6, 8, 9, 11, 14, 15, 17, 20, 22, 25, 28, 31, 39]
+    nine = [0, 2, 4, 6, 8, 10, 12, 14, 16, 18] + [-1] * 7
+    paths = np.array([full, nine, [0] + [-1] * 16], dtype=np.int32)
+    Ls = np.array([16, 9, 0], dtype=np.int32)
     seq = torch.full((b,), P, dtype=torch.int32, device=DEV)
     Kd, Vd = Kc.to(DEV), Vc.to(DEV)
     M.medusa_kv_compact(Kd, Vd, seq, torch.from_numpy(paths).to(DEV), torch.from_numpy(Ls).to(DEV))
