@@ -57,24 +57,6 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// LDS DMA (gfx950 global_load_lds_dwordx4): each lane's 16 bytes from its own
-// global address land at LDS byte m0 + 16 * lane.  The compiler does not see
-// this write: the caller waits with vm_wait<N>() and a barrier before any
-// wave reads the destination.  M0 is set in the same statement, one wait state
-// ahead of its use.  The 64-bit address register is consumed at issue.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
-
 constexpr int kWaves = 8;           // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT2 = 64;            // keys per tile

@@ -30,7 +30,7 @@
 //                 starts its K walk at its own chunk, so the workgroups do not
 //                 all read the same slice of X at once.  Tiles are mapped to
 //                 XCDs so that the M-tiles of one weight tile run on one XCD.
-//   gemm_big    : M > 80, MFMA-bound (see below).
+//   gemm_ring   : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
 #include <type_traits>
@@ -331,24 +331,32 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
   if (tm == 0) epi.copy_base(tn * BN, tn * BN + BN);
 }
 
-// ---------------------------------------------------------------- big-M bf16
-// MFMA-bound shape (hundreds to thousands of activation rows, e.g. the
-// verify rows of a batch).  Workgroup tile: BN = 32*WNB weight rows x
-// BM = 32*WMB activation rows; 2x2 waves, each 16*WNB x 16*WMB.  Both
-// operands are staged through double-buffered LDS in 64-wide K slices, rows
-// of 128 B with 16-byte chunks XOR-swizzled by (row >> 1) & 7 so the MFMA
-// fragment reads are free of bank conflicts.  One barrier per K slice; the
-// next slice is in registers while the current one is multiplied.
-template <int WMB, int WNB, class Epi>
-__global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict__ X, int64_t ldx,
-                                                     int M, const uint16_t* __restrict__ W, int N,
-                                                     int Kd, int ntm, Epi epi) {
-  constexpr int BM = 32 * WMB, BN = 32 * WNB, BK = 64;
-  constexpr int XP = BM * 8 / 256, WP = BN * 8 / 256;   // 16-byte pieces per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t wsm[2][BN * BK];
+// ---------------------------------------------------------------- MFMA-bound, LDS ring
+// Tile BM = 32*WMB activation rows x BN = 16*WNB*NWN weight rows; waves 2
+// (along M) x NWN (along N), each 16*WMB x 16*WNB outputs.  The operands
+// stream in 32-wide K slices through a 4-deep LDS ring filled by direct
+// global->LDS loads: three slices are in flight while one is multiplied, with
+// no staging registers.  A slice row is 64 bytes; its four 16-byte chunks are
+// XOR-swizzled by (row >> 2) & 3, so the fragment reads of 8 consecutive lanes
+// (8 rows, one chunk each) hit distinct banks.  One barrier per slice.
+// Each DMA issue fills a 1 KB region (16 rows x 64 bytes); the regions of a
+// slice go round-robin to the 4 waves (a wave short of a region repeats the
+// last one, writing identical bytes), so every wave issues the same count.
+template <int WMB, int WNB, int NWN, class Epi>
+__global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __restrict__ X,
+                                                           int64_t ldx, int M,
+                                                           const uint16_t* __restrict__ W, int N,
+                                                           int Kd, int ntm, Epi epi) {
+  constexpr int NW = 2 * NWN;                        // waves: 2 along M x NWN along N
+  constexpr int BM = 32 * WMB, BN = 16 * WNB * NWN, BK = 32, NS = 4;
+  constexpr int XR = BM / 16, WR = BN / 16;          // 1 KB regions per slice
+  constexpr int XPW = (XR + NW - 1) / NW, WPW = (WR + NW - 1) / NW;
+  constexpr int D = XPW + WPW;                       // DMA issues per wave per slice
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NS][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t wsm[NS][BN * BK];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
@@ -356,34 +364,34 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict_
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = Kd / BK;
 
-  const uint16_t* xsrc[XP];
-  const uint16_t* wsrc[WP];
-  int xdst[XP], wdst[WP];
+  const uint16_t* xsrc[XPW];
+  const uint16_t* wsrc[WPW];
+  uint32_t xoff[XPW], woff[WPW];
 #pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    const int p = threadIdx.x + 256 * i, row = p >> 3, ch = p & 7;
-    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch;
-    xdst[i] = row * BK + 8 * (ch ^ ((row >> 1) & 7));
+  for (int j = 0; j < XPW; ++j) {
+    const int r = min(wave + NW * j, XR - 1);
+    const int row = 16 * r + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch;
+    xoff[j] = (uint32_t)(r * 1024);
   }
 #pragma unroll
-  for (int i = 0; i < WP; ++i) {
-    const int p = threadIdx.x + 256 * i, row = p >> 3, ch = p & 7;
-    wsrc[i] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ch;
-    wdst[i] = row * BK + 8 * (ch ^ ((row >> 1) & 7));
+  for (int j = 0; j < WPW; ++j) {
+    const int r = min(wave + NW * j, WR - 1);
+    const int row = 16 * r + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    wsrc[j] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ch;
+    woff[j] = (uint32_t)(r * 1024);
   }
-  uint4 xr[XP], wr[WP];
-  auto load = [&](int kt) {
+  const uint32_t xl = lds_u32(&xs[0][0]), wl = lds_u32(&wsm[0][0]);
+  auto issue = [&](int kt, int buf) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < XP; ++i) xr[i] = ldg16(xsrc[i] + k0);
+    for (int j = 0; j < XPW; ++j)
+      dma16(xsrc[j] + k0, __builtin_amdgcn_readfirstlane(xl + (uint32_t)(buf * BM * BK * 2) + xoff[j]));
 #pragma unroll
-    for (int i = 0; i < WP; ++i) wr[i] = ldg16(wsrc[i] + k0);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XP; ++i) *reinterpret_cast<uint4*>(&xs[buf][xdst[i]]) = xr[i];
-#pragma unroll
-    for (int i = 0; i < WP; ++i) *reinterpret_cast<uint4*>(&wsm[buf][wdst[i]]) = wr[i];
+    for (int j = 0; j < WPW; ++j)
+      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(wl + (uint32_t)(buf * BN * BK * 2) + woff[j]));
   };
 
   f32x4 acc[WNB][WMB];
@@ -393,40 +401,35 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(const uint16_t* __restrict_
     for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int buf) {
+    uint4 a[WNB], bx[WMB];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint4 a[WNB], bx[WMB];
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) {
-        const int row = wn * 16 * WNB + 16 * nb + r16;
-        a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * ((4 * kk + g4) ^ ((row >> 1) & 7))]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < WMB; ++mb) {
-        const int row = wm * 16 * WMB + 16 * mb + r16;
-        bx[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * ((4 * kk + g4) ^ ((row >> 1) & 7))]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = mfma16x16x32(a[nb], bx[mb], acc[nb][mb]);
+    for (int nb = 0; nb < WNB; ++nb) {
+      const int row = wn * 16 * WNB + 16 * nb + r16;
+      a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * (g4 ^ ((row >> 2) & 3))]);
     }
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int row = wm * 16 * WMB + 16 * mb + r16;
+      bx[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * (g4 ^ ((row >> 2) & 3))]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = mfma16x16x32(a[nb], bx[mb], acc[nb][mb]);
   };
 
-  const int kl = nk - 1;
-  load(0);
-  store(0);
-  load(min(1, kl));
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nk) issue(i, i);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    __builtin_amdgcn_sched_barrier(0);
-    compute(buf);
-    __builtin_amdgcn_sched_barrier(0);
-    store(buf ^ 1);                  // slice kt + 1 (a repeat of the last one at the end)
-    load(min(kt + 2, kl));
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    // slices issued after slice kt so far: min(nk - 1 - kt, NS - 2), D issues each
+    const int ahead = min(nk - 1 - kt, NS - 2);
+    if (ahead >= 2) vm_wait<2 * D>();
+    else if (ahead == 1) vm_wait<D>();
+    else vm_wait<0>();
+    __syncthreads();   // slice kt complete from every wave; slice kt-1's buffer is free
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    compute(kt % NS);
   }
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb)
@@ -511,16 +514,41 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     else TILED_NW(MB_, (MB_ > 5 ? 8 : 16));                                                    \
   } while (0)
   if constexpr (std::is_same<Epi, EpiLogits>::value) if (mb > 5 && (Kd % 64) == 0) {
-    // MFMA-bound: 256 weight rows x 224 or 256 activation rows per workgroup,
-    // whichever covers M with fewer padded rows
-    const int t7 = (M + 223) / 224, t8 = (M + 255) / 256;
-    const int ntn = (N + 255) / 256;
-    if (t7 * 224 < t8 * 256)
-      hipLaunchKernelGGL((gemm_big_bf16<7, 8, Epi>), dim3(t7 * ntn), dim3(256), 0, st, X, ldx, M, W,
-                         N, Kd, t7, epi);
-    else
-      hipLaunchKernelGGL((gemm_big_bf16<8, 8, Epi>), dim3(t8 * ntn), dim3(256), 0, st, X, ldx, M, W,
-                         N, Kd, t8, epi);
+    // MFMA-bound: 8-wave ring kernel.  One workgroup fits a CU, so the tile
+    // (BM = 128..256 rows x BN = 256 or 320 weight rows) minimises
+    // (rounds of 256 workgroups) x (tile area); the time per unit of tile area
+    // was measured to be nearly the same across these tiles.
+    int best_wmb = 7, best_wnb = 5;
+    long best = -1;
+    for (int wmb = 4; wmb <= 8; ++wmb)
+      for (int wnb = 4; wnb <= 5; ++wnb) {
+        const long tm = (M + 32 * wmb - 1) / (32 * wmb), tn = (N + 64 * wnb - 1) / (64 * wnb);
+        const long cost = ((tm * tn + 255) / 256) * (32L * wmb) * (64L * wnb);
+        if (best < 0 || cost < best || (cost == best && wmb * wnb > best_wmb * best_wnb)) {
+          best = cost;
+          best_wmb = wmb;
+          best_wnb = wnb;
+        }
+      }
+#define RING(WMB_, WNB_)                                                                        \
+  do {                                                                                          \
+    const int tm = (M + 32 * WMB_ - 1) / (32 * WMB_), tn = (N + 64 * WNB_ - 1) / (64 * WNB_);   \
+    hipLaunchKernelGGL((gemm_ring_bf16<WMB_, WNB_, 4, Epi>), dim3(tm * tn), dim3(512), 0, st, X, \
+                       ldx, M, W, N, Kd, tm, epi);                                              \
+  } while (0)
+    switch (best_wmb * 10 + best_wnb) {
+      case 44: RING(4, 4); break;
+      case 45: RING(4, 5); break;
+      case 54: RING(5, 4); break;
+      case 55: RING(5, 5); break;
+      case 64: RING(6, 4); break;
+      case 65: RING(6, 5); break;
+      case 74: RING(7, 4); break;
+      case 75: RING(7, 5); break;
+      case 84: RING(8, 4); break;
+      default: RING(8, 5); break;
+    }
+#undef RING
     return hipGetLastError();
   }
   switch (mb) {

@@ -86,7 +86,8 @@ def test_zero_head_weights_reduce_to_base_head_bitwise(dt):
                                        (2080, 384, 1000), (300, 128, 777), (97, 512, 300),
                                        (5, 384, 31000), (65, 256, 30977), (16, 640, 33000),
                                        (80, 128, 30720), (5, 256, 40000), (65, 128, 50000),
-                                       (16, 256, 60000)])
+                                       (16, 256, 60000), (161, 128, 40001),
+                                       (1040, 384, 3333)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
