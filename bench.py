@@ -4,7 +4,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 heads + LM projection, shortlists, tree, tree attention, verify logits,
 acceptance, KV compaction (five library calls: shortlists + tree and acceptance
-+ compaction each run as one fused call, see speculative_decoding_heads_amd/step.py).
++ compaction each run as one fused call, and the verify logits leave the
+acceptance statistics behind; see speculative_decoding_heads_amd/step.py).
 Default workload: the Llama-7B shape at batch 1 (hidden 4096, vocab 32000,
 4 heads, 64-candidate tree, 32 heads x 128, prefix 2048, bf16, greedy); the
 batch-16 typical-acceptance variant is measured too and reported alongside.
@@ -51,7 +52,7 @@ def alg_bytes(c):
         "topk_tree": rows_d * c.V * 4 + c.b * c.T * 8,
         "tree_attn": 2 * c.b * c.nkv * (c.P + c.T) * c.d * e + 2 * c.b * c.T * c.nq * c.d * e,
         "verify_lm": c.V * c.H * e + rows_v * c.H * e + rows_v * c.V * 4,
-        "accept_compact": rows_v * c.V * 4 + 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
+        "accept_compact": 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
     }
 
 
@@ -77,12 +78,14 @@ def _enqueue(st, x, step, M, c, ev=None):
     mark(2)
     M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
     mark(3)
-    M.medusa_heads(st.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
-                   st.base_logits.view(c.b * c.T, c.V), include_base=1)
+    M.medusa_verify_logits(st.O.view(c.b * c.T, c.nq * c.d), x["LM"],
+                           st.base_logits.view(c.b * c.T, c.V), st.mode, c.temperature,
+                           st.ws_verify)
     mark(4)
     M.medusa_accept_compact(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode,
                             c.temperature, c.eps, c.delta, c.seed, step, st.L, st.path,
-                            st.acc_tokens, st.bonus, x["Kc"], x["Vc"], x["seq_len"], st.ws_acc)
+                            st.acc_tokens, st.bonus, x["Kc"], x["Vc"], x["seq_len"], st.ws_acc,
+                            verify_ws=st.ws_verify)
     mark(5)
 
 

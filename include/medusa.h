@@ -235,17 +235,42 @@ int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
  * the rollback done by the acceptance walk's own workgroup (one launch less).
  * Arguments: those of medusa_accept, then the cache arguments of
  * medusa_kv_compact (Kc, Vc [b, nkv, Pmax, d] dtype, seq_len [b] device, in:
- * P, out: P + L + 1; K is medusa_accept's K).  Outputs are bit-identical to
- * the two calls in sequence.  Errors: the union of both calls' checks;
- * nothing is launched on error.
+ * P, out: P + L + 1; K is medusa_accept's K), then verify_ws: NULL, or the
+ * workspace of the medusa_verify_logits call that wrote base_logits (same
+ * rows b*T, V, mode and temperature); with it the per-node argmax /
+ * softmax statistics come from its partials instead of a pass over
+ * base_logits.  The statistics then differ only in float32 rounding, so the
+ * outputs are the same except for a node whose typical-acceptance margin is
+ * within that rounding.  Errors: the union of both calls' checks; nothing is
+ * launched on error.
  * ------------------------------------------------------------------------- */
 int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const int32_t* parent,
                           const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K,
                           int32_t mode, float temperature, float eps, float delta, uint64_t seed,
                           uint64_t step, int32_t* L, int32_t* path, int32_t* acc_tokens,
                           int32_t* bonus, void* Kc, void* Vc, int32_t* seq_len, int32_t nkv,
-                          int32_t Pmax, int32_t d, int32_t dtype, void* ws, size_t ws_bytes,
-                          void* stream);
+                          int32_t Pmax, int32_t d, int32_t dtype, const void* verify_ws,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_verify_logits - the verify-rows LM projection of medusa_heads
+ * (n_heads = 0, include_base = 1: logits [rows, V] f32 = x [rows, H] . LM^T)
+ * that also leaves, in ws, the acceptance statistics of every row per weight
+ * tile: the argmax key (GREEDY) or the online softmax statistics of
+ * logits / temperature (TYPICAL).  medusa_accept_compact consumes them
+ * (verify_ws), so acceptance does not re-read the logits.  Below 2^24 logits
+ * (rows * V) re-reading is cheaper: then no partials are kept and
+ * medusa_accept_compact reads the logits as without verify_ws.  [glossary]
+ * verification phase: the original output head scores every candidate.
+ *   x [rows, H], LM [V, H] (dtype); logits [rows, V] f32, as medusa_heads.
+ *   ws: medusa_verify_workspace(rows, H, V, dtype, mode) bytes, 16-byte
+ *       aligned, device, caller-owned; contents are opaque.
+ * logits are bit-identical to medusa_heads.  Errors as medusa_heads.
+ * ------------------------------------------------------------------------- */
+size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode);
+int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
+                         int32_t dtype, int32_t mode, float temperature, float* logits, void* ws,
+                         size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

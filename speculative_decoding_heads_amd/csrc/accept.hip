@@ -32,45 +32,6 @@
 
 namespace medusa {
 
-struct Stat {
-  float m, s, t, pad;
-};
-
-__device__ __forceinline__ void stat_add(float& m, float& s, float& t, float x) {
-  if (x <= m) {
-    const float d = x - m;
-    const float e = expf(d);
-    s += e;
-    t = fmaf(e, d, t);
-  } else {
-    if (s > 0.f) {
-      const float d = m - x;          // < 0
-      const float r = expf(d);
-      t = r * fmaf(d, s, t);
-      s = fmaf(r, s, 1.f);
-    } else {
-      s = 1.f;
-      t = 0.f;
-    }
-    m = x;
-  }
-}
-
-__device__ __forceinline__ void stat_merge(float& m, float& s, float& t, float m2, float s2,
-                                           float t2) {
-  if (s2 == 0.f) return;
-  if (s == 0.f) {
-    m = m2; s = s2; t = t2;
-    return;
-  }
-  const float M = fmaxf(m, m2);
-  const float d1 = m - M, d2 = m2 - M;
-  const float r1 = expf(d1), r2 = expf(d2);
-  t = r1 * fmaf(d1, s, t) + r2 * fmaf(d2, s2, t2);
-  s = r1 * s + r2 * s2;
-  m = M;
-}
-
 constexpr int kStatThreads = 1024;
 
 // One 1024-thread workgroup per node row; each lane issues a group of 16-byte
@@ -80,7 +41,7 @@ template <int MODE>
 __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __restrict__ logits,
                                                              int V, float inv_temp,
                                                              int* __restrict__ amax,
-                                                             Stat* __restrict__ stats) {
+                                                             RowStat* __restrict__ stats) {
   const int64_t row = blockIdx.x;
   const float* x = logits + row * V;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -139,7 +100,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __rest
     if (tid == 0) {
       float M = sm[0][0], S = sm[0][1], Tt = sm[0][2];
       for (int w = 1; w < NW; ++w) stat_merge(M, S, Tt, sm[w][0], sm[w][1], sm[w][2]);
-      stats[row] = Stat{M, S, Tt, 0.f};
+      stats[row] = RowStat{M, S, Tt, 0.f};
     }
   }
 }
@@ -156,27 +117,88 @@ __device__ __forceinline__ bool full_path(int c, const int* sparent, const unsig
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ logits,
+__global__ __launch_bounds__(1024) void accept_walk(const float* __restrict__ logits,
                                                    const int* __restrict__ tokens,
                                                    const int* __restrict__ parent,
                                                    const int* __restrict__ depth, int T, int V,
                                                    int K, float inv_temp, float eps, float delta,
                                                    const int* __restrict__ amax,
-                                                   const Stat* __restrict__ stats,
+                                                   const RowStat* __restrict__ stats,
                                                    int* __restrict__ Lout, int* __restrict__ path,
                                                    int* __restrict__ acc_tokens,
                                                    int* __restrict__ bonus, int* __restrict__ best_out,
                                                    uint8_t* __restrict__ Kc, uint8_t* __restrict__ Vc,
                                                    int* __restrict__ seq_len, int nkv, int Pmax,
-                                                   int row_bytes) {
+                                                   int row_bytes, const int* __restrict__ parts_hdr,
+                                                   const uint64_t* __restrict__ pkey,
+                                                   const RowStat* __restrict__ pstat) {
   const int s = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int spath[kMaxHeads + 1];
   const int P = Kc ? seq_len[s] : 0;
   __shared__ unsigned char local[kMaxT];
   __shared__ int sdepth[kMaxT], sparent[kMaxT];
+  __shared__ int samax[kMaxT];
+  __shared__ RowStat sstat[kMaxT];
   __shared__ int bestL, bestNode;
   if (tid == 0) { bestL = 0; bestNode = 0x7fffffff; }
+  // per-node statistics of this sequence: from the verify GEMM's partials
+  // (one wave per node row, lanes over the weight tiles), or per row as given
+  if (parts_hdr) {
+    const int ntiles = parts_hdr[0];
+    const int nw = blockDim.x / 64;
+    // four rows of a wave at a time, four tiles per lane and row in flight
+    constexpr int RR = 4;
+    for (int p0 = wave; p0 < T; p0 += RR * nw) {
+      RowPart acc2[RR];
+#pragma unroll
+      for (int rr = 0; rr < RR; ++rr) part_init(acc2[rr]);
+      for (int j0 = 0; j0 < ntiles; j0 += 4 * 64) {
+        RowPart q[RR][4];
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int p = min(p0 + rr * nw, T - 1), j = j0 + u * 64 + lane;
+            const int64_t o = ((int64_t)s * T + p) * ntiles + min(j, ntiles - 1);
+            const bool ok = j < ntiles;
+            if (MODE == kGreedy) {
+              q[rr][u].key = ok ? pkey[o] : 0ull;
+            } else {
+              const RowStat st = pstat[o];
+              q[rr][u].m = st.m;
+              q[rr][u].s = ok ? st.s : 0.f;
+              q[rr][u].t = st.t;
+            }
+          }
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) part_merge(acc2[rr], q[rr][u], MODE == kTypical);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RR; ++rr) {
+        if (MODE == kGreedy) {
+          acc2[rr].key = wave_max_u64(acc2[rr].key);
+        } else {
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) part_xor(acc2[rr], o, true);
+        }
+        const int p = p0 + rr * nw;
+        if (lane == 0 && p < T) {
+          samax[p] = (int)key_index(acc2[rr].key);
+          sstat[p] = RowStat{acc2[rr].m, acc2[rr].s, acc2[rr].t, 0.f};
+        }
+      }
+    }
+  } else {
+    for (int p = tid; p < T; p += blockDim.x) {
+      const int64_t row = (int64_t)s * T + p;
+      if (MODE == kGreedy) samax[p] = amax[row];
+      else sstat[p] = stats[row];
+    }
+  }
+  __syncthreads();
   for (int c = tid; c < T; c += blockDim.x) {
     sparent[c] = parent[c];
     sdepth[c] = depth[c];
@@ -187,9 +209,9 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
       const int64_t prow = (int64_t)s * T + p;
       if (tok >= 0 && tok < V && p >= 0 && p < c) {
         if (MODE == kGreedy) {
-          ok = tok == amax[prow];
+          ok = tok == samax[p];
         } else {
-          const Stat st = stats[prow];
+          const RowStat st = sstat[p];
           const double lns = log((double)st.s);
           const double H = lns - (double)st.t / (double)st.s;
           const double logq = (double)(logits[prow * V + tok] * inv_temp) - (double)st.m - lns;
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
       acc_tokens[(int64_t)s * (K + 1) + d] = tokens[(int64_t)s * T + a];
       a = a > 0 ? sparent[a] : 0;
     }
-    if (MODE == kGreedy) bonus[s] = amax[(int64_t)s * T + best];
+    if (MODE == kGreedy) bonus[s] = samax[best];
     best_out[s] = best;
   }
   if (!Kc) return;
@@ -241,15 +263,16 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
 size_t accept_workspace(int b, int T) {
   // amax / stats per node row, plus the chosen node per sequence
   size_t rows = (size_t)b * T;
-  return rows * sizeof(Stat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 64;
+  return rows * sizeof(RowStat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 64;
 }
 
 hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
                       const int* depth, int b, int T, int V, int K, int mode, float temperature,
                       float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
-                      int* acc_tokens, int* bonus, void* ws, hipStream_t st, const KvRollback* kv) {
+                      int* acc_tokens, int* bonus, void* ws, hipStream_t st, const KvRollback* kv,
+                      const void* parts) {
   const size_t rows = (size_t)b * T;
-  Stat* stats = static_cast<Stat*>(ws);
+  RowStat* stats = static_cast<RowStat*>(ws);
   int* amax = reinterpret_cast<int*>(stats + rows);
   int* best = amax + rows;
   const float inv_temp = 1.0f / temperature;
@@ -258,19 +281,27 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   int* seq_len = kv ? kv->seq_len : nullptr;
   const int nkv = kv ? kv->nkv : 0, Pmax = kv ? kv->Pmax : 0;
   const int row_bytes = kv ? kv->d * (kv->dtype == kBF16 ? 2 : 4) : 0;
+  const int* hdr = static_cast<const int*>(parts);
+  const uint64_t* pkey =
+      parts ? reinterpret_cast<const uint64_t*>(static_cast<const char*>(parts) + kPartsHeader) : nullptr;
+  const RowStat* pstat =
+      parts ? reinterpret_cast<const RowStat*>(static_cast<const char*>(parts) + kPartsHeader) : nullptr;
   if (mode == kGreedy) {
-    hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
-                       V, inv_temp, amax, stats);
-    hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
+    if (!parts)
+      hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
+                         base_logits, V, inv_temp, amax, stats);
+    hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(parts ? 1024 : 256), 0, st, base_logits, tokens,
                        parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
-                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, hdr, pkey,
+                       pstat);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st, base_logits,
-                     V, inv_temp, amax, stats);
-  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
+  if (!parts)
+    hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
+                       base_logits, V, inv_temp, amax, stats);
+  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(parts ? 1024 : 256), 0, st, base_logits, tokens, parent,
                      depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,
-                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
+                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, hdr, pkey, pstat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,

@@ -109,6 +109,40 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
                     "LM projection");
 }
 
+// ------------------------------------------------------------------- verify logits + partials
+size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode) {
+  if (rows <= 0 || H <= 0 || V <= 0 || !dtype_ok(dtype)) return 0;
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL) return 0;
+  if (rows > INT32_MAX / 2) return 0;
+  return round_up(verify_workspace((int)rows, V, H, dtype, mode));
+}
+
+int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
+                         int32_t dtype, int32_t mode, float temperature, float* logits, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (rows < 0) return fail(MEDUSA_ERR_ARG, "rows < 0");
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (H <= 0 || V <= 0) return fail(MEDUSA_ERR_ARG, "H and V must be positive");
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
+  if (mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  if (rows == 0) return MEDUSA_OK;
+  if (!x || !LM || !logits) return fail(MEDUSA_ERR_ARG, "x, LM and logits must be non-NULL");
+  if (rows > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "too many rows");
+  if (dtype == MEDUSA_BF16) {
+    if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "bf16 rows need H % 128 == 0");
+    if (!aligned16(x) || !aligned16(LM)) return fail(MEDUSA_ERR_ARG, "bf16 operands must be 16-byte aligned");
+  }
+  const size_t need = medusa_verify_workspace(rows, H, V, dtype, mode);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "verify: workspace too small");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
+  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
+  return hip_status(run_verify_logits(x, (int)rows, H, LM, V, dtype, logits, mode, tmp, ws,
+                                      as_stream(stream)),
+                    "verify logits");
+}
+
 // ------------------------------------------------------------------- top-k
 size_t medusa_topk_workspace(int32_t b, int32_t K, int32_t V, int32_t kmax) {
   if (b <= 0 || K <= 0 || V <= 0 || kmax <= 0) return 0;
@@ -331,8 +365,8 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
                           int32_t mode, float temperature, float eps, float delta, uint64_t seed,
                           uint64_t step, int32_t* L, int32_t* path, int32_t* acc_tokens,
                           int32_t* bonus, void* Kc, void* Vc, int32_t* seq_len, int32_t nkv,
-                          int32_t Pmax, int32_t d, int32_t dtype, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          int32_t Pmax, int32_t d, int32_t dtype, const void* verify_ws,
+                          void* ws, size_t ws_bytes, void* stream) {
   if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
   if (V < 1) return fail(MEDUSA_ERR_ARG, "V must be positive");
   if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
@@ -357,9 +391,10 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
   const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
   KvRollback kv{Kc, Vc, seq_len, nkv, Pmax, d, dtype};
+  const void* parts = verify_ws && verify_uses_parts((int64_t)b * T, V) ? verify_ws : nullptr;
   return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,
                                delta, seed, step, L, path, acc_tokens, bonus, ws,
-                               as_stream(stream), &kv),
+                               as_stream(stream), &kv, parts),
                     "accept_compact");
 }
 

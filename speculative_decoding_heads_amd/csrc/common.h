@@ -136,6 +136,48 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Online softmax statistics of a row x' (x' = logits / temperature):
+// m = max x', s = sum e^(x'-m), t = sum e^(x'-m) (x'-m).  Then the entropy is
+// H = ln s - t/s and log softmax(x')_i = x'_i - m - ln s.
+struct RowStat {
+  float m, s, t, pad;
+};
+
+__device__ __forceinline__ void stat_add(float& m, float& s, float& t, float x) {
+  if (x <= m) {
+    const float d = x - m;
+    const float e = expf(d);
+    s += e;
+    t = fmaf(e, d, t);
+  } else {
+    if (s > 0.f) {
+      const float d = m - x;          // < 0
+      const float r = expf(d);
+      t = r * fmaf(d, s, t);
+      s = fmaf(r, s, 1.f);
+    } else {
+      s = 1.f;
+      t = 0.f;
+    }
+    m = x;
+  }
+}
+
+__device__ __forceinline__ void stat_merge(float& m, float& s, float& t, float m2, float s2,
+                                           float t2) {
+  if (s2 == 0.f) return;
+  if (s == 0.f) {
+    m = m2; s = s2; t = t2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  const float d1 = m - M, d2 = m2 - M;
+  const float r1 = expf(d1), r2 = expf(d2);
+  t = r1 * fmaf(d1, s, t) + r2 * fmaf(d2, s2, t2);
+  s = r1 * s + r2 * s2;
+  m = M;
+}
+
 // ---- order-preserving key for (value desc, index asc) selection ---------------
 // key = ord(x) << 32 | (0xffffffff - idx); a larger key is a larger value, and
 // among equal values the lower index.  -0.0 is folded onto +0.0.  Key 0 is
@@ -154,6 +196,84 @@ __device__ __forceinline__ uint64_t make_key(float x, uint32_t idx) {
 }
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
 __device__ __forceinline__ float key_value(uint64_t k) { return ord_float((uint32_t)(k >> 32)); }
+
+// Acceptance partial of one row over a range of its columns: the argmax key
+// (greedy) or the online statistics of x' = x / temperature (typical).
+struct RowPart {
+  uint64_t key;
+  float m, s, t;
+};
+__device__ __forceinline__ void part_init(RowPart& p) {
+  p.key = 0;
+  p.m = -INFINITY;
+  p.s = 0.f;
+  p.t = 0.f;
+}
+__device__ __forceinline__ void part_add(RowPart& p, float v, int n, bool typical, float inv_temp) {
+  if (typical) {
+    stat_add(p.m, p.s, p.t, v * inv_temp);
+  } else {
+    const uint64_t k = make_key(v, (uint32_t)n);
+    p.key = k > p.key ? k : p.key;
+  }
+}
+__device__ __forceinline__ void part_merge(RowPart& p, const RowPart& q, bool typical) {
+  if (typical) stat_merge(p.m, p.s, p.t, q.m, q.s, q.t);
+  else p.key = q.key > p.key ? q.key : p.key;
+}
+// merge with the partial of lane ^ o (only the fields of the mode move)
+__device__ __forceinline__ void part_xor(RowPart& p, int o, bool typical) {
+  RowPart q;
+  if (typical) {
+    q.m = __shfl_xor(p.m, o, 64);
+    q.s = __shfl_xor(p.s, o, 64);
+    q.t = __shfl_xor(p.t, o, 64);
+  } else {
+    q.key = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(p.key >> 32), o, 64) << 32) |
+            (uint32_t)__shfl_xor((int)(uint32_t)p.key, o, 64);
+  }
+  part_merge(p, q, typical);
+}
+
+// Partial of NV values of one row held by a lane, at increasing columns col[k]
+// (columns >= N are ignored): greedy takes the largest value and then its
+// lowest column; typical forms (m, s, t) of x' = v / temperature in two passes
+// (max, then the sums) with the hardware exponential.
+template <int NV>
+__device__ __forceinline__ RowPart lane_part(const float (&v)[NV], const int (&col)[NV], int N,
+                                             bool typical, float inv_temp) {
+  RowPart p;
+  part_init(p);
+  float mx = -INFINITY;
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const bool ok = col[k] < N;
+    const float x = typical ? v[k] * inv_temp : v[k];
+    mx = ok ? fmaxf(mx, x) : mx;
+    any = any || ok;
+  }
+  if (!any) return p;
+  if (typical) {
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const float d = v[k] * inv_temp - mx;
+      const float e = col[k] < N ? __expf(d) : 0.f;
+      s += e;
+      t = fmaf(e, d, t);
+    }
+    p.m = mx;
+    p.s = s;
+    p.t = t;
+  } else {
+    int ci = 0;
+#pragma unroll
+    for (int k = NV - 1; k >= 0; --k) ci = (col[k] < N && v[k] == mx) ? col[k] : ci;
+    p.key = make_key(mx, (uint32_t)ci);
+  }
+  return p;
+}
 
 // ---- counter-based uniform draws (SplitMix64, Steele/Lea/Flood 2014) ---------
 __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {

@@ -60,6 +60,34 @@ struct EpiLogits {
   __device__ __forceinline__ void copy_base(int, int) const {}
 };
 
+// Logits plus the acceptance partial of every (row, weight tile): the argmax
+// key (greedy) or the online softmax statistics of logits / temperature
+// (typical), so acceptance never re-reads the logits for them.  Partials are
+// [rows][ntiles]; header = {ntiles, typical, rows}, written by workgroup 0.
+struct EpiLogitsStats : EpiLogits {
+  bool typical;
+  float inv_temp;
+  int ntiles;
+  int* header;
+  uint64_t* pkey;
+  RowStat* pstat;
+  __device__ __forceinline__ void write_part(int row, int tile, const RowPart& p) const {
+    const int64_t o = (int64_t)row * ntiles + tile;
+    if (typical) pstat[o] = RowStat{p.m, p.s, p.t, 0.f};
+    else pkey[o] = p.key;
+  }
+  __device__ __forceinline__ void write_header() const {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      header[0] = ntiles;
+      header[1] = typical ? 1 : 0;
+      header[2] = M;
+    }
+  }
+};
+template <class Epi> struct HasParts : std::false_type {};
+template <> struct HasParts<EpiLogitsStats> : std::true_type {};
+template <class Epi> struct IsLogits : std::is_base_of<EpiLogits, Epi> {};
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // u[m, base + i, o] = x[m, o] + SiLU(z[m, i*H + o])   (n = i*H + o)
@@ -329,6 +357,36 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 16 * nb + 4 * g4, acc[nb][mb]);
   if (tm == 0) epi.copy_base(tn * BN, tn * BN + BN);
+  if constexpr (HasParts<Epi>::value) {
+    // row partials over this workgroup's BN columns: lanes (4 columns each),
+    // then the 4 lane groups of a row (shuffles), then the waves (LDS)
+    __syncthreads();                        // every wave is past its last read of xs
+    RowPart* red = reinterpret_cast<RowPart*>(&xs[0][0]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float v[4 * NBW];
+      int col[4 * NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[4 * nb + i] = acc[nb][mb][i];
+          col[4 * nb + i] = n0 + 16 * nb + 4 * g4 + i;
+        }
+      RowPart pt = lane_part(v, col, N, epi.typical, epi.inv_temp);
+      part_xor(pt, 16, epi.typical);
+      part_xor(pt, 32, epi.typical);
+      if (g4 == 0) red[wave * BM + 16 * mb + r16] = pt;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+      if (m0 + r >= M) continue;
+      RowPart pt = red[r];
+      for (int w = 1; w < NWAVES; ++w) part_merge(pt, red[w * BM + r], epi.typical);
+      epi.write_part(m0 + r, tn, pt);
+    }
+    epi.write_header();
+  }
 }
 
 // ---------------------------------------------------------------- MFMA-bound, LDS ring
@@ -437,6 +495,36 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
     for (int mb = 0; mb < WMB; ++mb)
       epi.store4(m0 + wm * 16 * WMB + 16 * mb + r16, n0 + wn * 16 * WNB + 16 * nb + 4 * g4,
                  acc[nb][mb]);
+  if constexpr (HasParts<Epi>::value) {
+    // row partials over this workgroup's BN columns (lanes, lane groups, the
+    // NWN waves along N)
+    __syncthreads();                        // every wave is past its last read of xs
+    RowPart* red = reinterpret_cast<RowPart*>(&xs[0][0]);
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      float v[4 * WNB];
+      int col[4 * WNB];
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[4 * nb + i] = acc[nb][mb][i];
+          col[4 * nb + i] = n0 + wn * 16 * WNB + 16 * nb + 4 * g4 + i;
+        }
+      RowPart pt = lane_part(v, col, N, epi.typical, epi.inv_temp);
+      part_xor(pt, 16, epi.typical);
+      part_xor(pt, 32, epi.typical);
+      if (g4 == 0) red[wn * BM + wm * 16 * WMB + 16 * mb + r16] = pt;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += 128 * NWN) {
+      if (m0 + r >= M) continue;
+      RowPart pt = red[r];
+      for (int w = 1; w < NWN; ++w) part_merge(pt, red[w * BM + r], epi.typical);
+      epi.write_part(m0 + r, tn, pt);
+    }
+    epi.write_header();
+  }
 }
 
 // ---------------------------------------------------------------- f32
@@ -478,65 +566,80 @@ __global__ void copy_base_rows(T* U, const T* X, int64_t ldx, int M, int H, int 
 }
 
 // ---------------------------------------------------------------- launchers
-template <class Epi>
-static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
-                              int Kd, const Epi& epi, hipStream_t st) {
+// Kernel choice for a bf16 GEMM (M activation rows, N weight rows, K = Kd).
+struct Bf16Plan {
+  int kind;      // 0 skinny, 1 tiled, 2 ring
+  int mb;        // tiled: 16-row activation blocks per workgroup
+  int nw;        // tiled: waves per workgroup
+  int wmb, wnb;  // ring: tile parameters
+  int ntiles;    // workgroup tiles along N
+};
+
+static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
+  Bf16Plan p{};
   const int mb = (M + 15) / 16;
   // 8-wave tiled workgroups own 128 weight rows: with enough rows to give
   // every CU one, they stream best; otherwise skinny (up to 16 rows) or
   // 4-wave tiled workgroups keep more of them in flight.
   const bool wide = N >= 240 * 128;
-  if (!wide && M <= 16) {
-    // skinny: 4 waves split K, X (a few rows) read from L2
-    hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3((N + 31) / 32), dim3(256), 0, st, X, ldx,
-                       M, W, N, Kd, epi);
-    return hipGetLastError();
+  if (skinny_ok && !wide && M <= 16) {
+    p.kind = 0;
+    p.ntiles = (N + 31) / 32;
+    return p;
   }
-  // Wide weights: 8-wave workgroups of 128 rows; when that leaves a partial
-  // last round of workgroups on the 256 CUs (N between 2048 and 4096 16-row
-  // blocks), 10/12/16-wave workgroups make exactly one round instead.
-  const int units = (N + 15) / 16;
-  const int nw = units <= 8 * 256 || units > 16 * 256 ? 8
-                 : units <= 10 * 256 ? 10 : units <= 12 * 256 ? 12 : 16;
-#define TILED_NW(MB_, NW_)                                                                     \
-  do {                                                                                         \
-    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
-    const int ntn = (N + 16 * NW_ - 1) / (16 * NW_);                                           \
-    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * ntn), dim3(64 * NW_), 0, \
-                       st, X, ldx, M, W, N, Kd, ntm, epi);                                     \
-  } while (0)
-#define TILED(MB_, NBW_)                                                                       \
-  do {                                                                                         \
-    if (!wide) TILED_NW(MB_, 4);                                                               \
-    else if (MB_ > 5 || nw == 8) TILED_NW(MB_, 8);                                             \
-    else if (nw == 10) TILED_NW(MB_, (MB_ > 5 ? 8 : 10));                                      \
-    else if (nw == 12) TILED_NW(MB_, (MB_ > 5 ? 8 : 12));                                      \
-    else TILED_NW(MB_, (MB_ > 5 ? 8 : 16));                                                    \
-  } while (0)
-  if constexpr (std::is_same<Epi, EpiLogits>::value) if (mb > 5 && (Kd % 64) == 0) {
+  if (logits && mb > 5 && (Kd % 64) == 0) {
     // MFMA-bound: 8-wave ring kernel.  One workgroup fits a CU, so the tile
     // (BM = 128..256 rows x BN = 256 or 320 weight rows) minimises
-    // (rounds of 256 workgroups) x (tile area); the time per unit of tile area
-    // was measured to be nearly the same across these tiles.
-    int best_wmb = 7, best_wnb = 5;
+    // (rounds of 256 workgroups) x (tile area); the time per unit of tile
+    // area was measured to be nearly the same across these tiles.
+    p.kind = 2;
     long best = -1;
     for (int wmb = 4; wmb <= 8; ++wmb)
       for (int wnb = 4; wnb <= 5; ++wnb) {
         const long tm = (M + 32 * wmb - 1) / (32 * wmb), tn = (N + 64 * wnb - 1) / (64 * wnb);
         const long cost = ((tm * tn + 255) / 256) * (32L * wmb) * (64L * wnb);
-        if (best < 0 || cost < best || (cost == best && wmb * wnb > best_wmb * best_wnb)) {
+        if (best < 0 || cost < best || (cost == best && wmb * wnb > p.wmb * p.wnb)) {
           best = cost;
-          best_wmb = wmb;
-          best_wnb = wnb;
+          p.wmb = wmb;
+          p.wnb = wnb;
         }
       }
+    p.ntiles = (N + 64 * p.wnb - 1) / (64 * p.wnb);
+    return p;
+  }
+  p.kind = 1;
+  p.mb = mb <= 6 ? mb : mb <= 8 ? 8 : mb <= 10 ? 10 : 8;
+  // Wide weights: 8-wave workgroups of 128 rows; when that leaves a partial
+  // last round of workgroups on the 256 CUs (N between 2048 and 4096 16-row
+  // blocks), 10/12/16-wave workgroups make exactly one round instead.
+  const int units = (N + 15) / 16;
+  if (!wide) p.nw = 4;
+  else if (p.mb > 5 || units <= 8 * 256 || units > 16 * 256) p.nw = 8;
+  else p.nw = units <= 10 * 256 ? 10 : units <= 12 * 256 ? 12 : 16;
+  p.ntiles = (N + 16 * p.nw - 1) / (16 * p.nw);
+  return p;
+}
+
+template <class Epi>
+static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
+                              int Kd, const Epi& epi, hipStream_t st) {
+  // logits always take the tiled / ring kernels, so the verify-rows logits of
+  // medusa_heads and medusa_verify_logits come from the same kernel
+  const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
+  if (p.kind == 0) {
+    // skinny: 4 waves split K, X (a few rows) read from L2
+    hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx, M,
+                       W, N, Kd, epi);
+    return hipGetLastError();
+  }
+  if constexpr (IsLogits<Epi>::value) if (p.kind == 2) {
 #define RING(WMB_, WNB_)                                                                        \
   do {                                                                                          \
-    const int tm = (M + 32 * WMB_ - 1) / (32 * WMB_), tn = (N + 64 * WNB_ - 1) / (64 * WNB_);   \
-    hipLaunchKernelGGL((gemm_ring_bf16<WMB_, WNB_, 4, Epi>), dim3(tm * tn), dim3(512), 0, st, X, \
-                       ldx, M, W, N, Kd, tm, epi);                                              \
+    const int tm = (M + 32 * WMB_ - 1) / (32 * WMB_);                                           \
+    hipLaunchKernelGGL((gemm_ring_bf16<WMB_, WNB_, 4, Epi>), dim3(tm * p.ntiles), dim3(512), 0,  \
+                       st, X, ldx, M, W, N, Kd, tm, epi);                                       \
   } while (0)
-    switch (best_wmb * 10 + best_wnb) {
+    switch (p.wmb * 10 + p.wnb) {
       case 44: RING(4, 4); break;
       case 45: RING(4, 5); break;
       case 54: RING(5, 4); break;
@@ -551,18 +654,29 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
 #undef RING
     return hipGetLastError();
   }
-  switch (mb) {
-    case 1: TILED(1, 1); break;
-    case 2: TILED(2, 1); break;
-    case 3: TILED(3, 1); break;
-    case 4: TILED(4, 1); break;
-    case 5: TILED(5, 1); break;
-    case 6: TILED(6, 1); break;
-    case 7:
-    case 8: TILED(8, 1); break;
-    case 9:
-    case 10: TILED(10, 1); break;
-    default: TILED(8, 1); break;
+#define TILED_NW(MB_, NW_)                                                                     \
+  do {                                                                                         \
+    const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * p.ntiles), dim3(64 * NW_), \
+                       0, st, X, ldx, M, W, N, Kd, ntm, epi);                                  \
+  } while (0)
+#define TILED(MB_)                                                                             \
+  do {                                                                                         \
+    if (p.nw == 4) TILED_NW(MB_, 4);                                                           \
+    else if (MB_ > 5 || p.nw == 8) TILED_NW(MB_, 8);                                           \
+    else if (p.nw == 10) TILED_NW(MB_, (MB_ > 5 ? 8 : 10));                                    \
+    else if (p.nw == 12) TILED_NW(MB_, (MB_ > 5 ? 8 : 12));                                    \
+    else TILED_NW(MB_, (MB_ > 5 ? 8 : 16));                                                    \
+  } while (0)
+  switch (p.mb) {
+    case 1: TILED(1); break;
+    case 2: TILED(2); break;
+    case 3: TILED(3); break;
+    case 4: TILED(4); break;
+    case 5: TILED(5); break;
+    case 6: TILED(6); break;
+    case 10: TILED(10); break;
+    default: TILED(8); break;
   }
 #undef TILED
 #undef TILED_NW
@@ -613,6 +727,82 @@ hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int
                        H, epi, st);
   return launch_f32(static_cast<const float*>(x), H, M, static_cast<const float*>(LM), V, H, epi,
                     st);
+}
+
+// ---------------------------------------------------------------- verify logits + partials
+// f32 rows (tiny workload): one 256-thread workgroup per row folds the whole
+// row into one partial (ntiles = 1).
+__global__ __launch_bounds__(256) void row_parts_f32(const float* __restrict__ logits, int M, int V,
+                                                     bool typical, float inv_temp,
+                                                     int* __restrict__ header,
+                                                     uint64_t* __restrict__ pkey,
+                                                     RowStat* __restrict__ pstat) {
+  const int row = blockIdx.x;
+  const float* x = logits + (int64_t)row * V;
+  RowPart pt;
+  part_init(pt);
+  for (int e = threadIdx.x; e < V; e += 256) part_add(pt, x[e], e, typical, inv_temp);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part_xor(pt, o, typical);
+  __shared__ RowPart red[4];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = pt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) part_merge(pt, red[w], typical);
+    if (typical) pstat[row] = RowStat{pt.m, pt.s, pt.t, 0.f};
+    else pkey[row] = pt.key;
+    if (row == 0) {
+      header[0] = 1;
+      header[1] = typical ? 1 : 0;
+      header[2] = M;
+    }
+  }
+}
+
+int verify_tiles(int M, int N, int Kd, int dtype) {
+  if (dtype != kBF16) return 1;
+  return plan_bf16(M, N, Kd, true, false).ntiles;
+}
+
+// Partials pay off when the logits are large (re-reading them for the
+// statistics costs more than merging the partials): from 2^24 logits.
+bool verify_uses_parts(int64_t M, int64_t N) { return M * N >= (int64_t)1 << 24; }
+
+size_t verify_workspace(int M, int N, int Kd, int dtype, int mode) {
+  if (!verify_uses_parts(M, N)) return kPartsHeader;
+  const size_t per = mode == kTypical ? sizeof(RowStat) : sizeof(uint64_t);
+  return kPartsHeader + (size_t)M * verify_tiles(M, N, Kd, dtype) * per;
+}
+
+hipError_t run_verify_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
+                             float* logits, int mode, float temperature, void* ws, hipStream_t st) {
+  if (!verify_uses_parts(M, V)) return run_lm_logits(x, M, H, LM, V, dtype, logits, st);
+  const bool typical = mode == kTypical;
+  const float inv_temp = 1.0f / temperature;
+  int* header = static_cast<int*>(ws);
+  uint64_t* pkey = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kPartsHeader);
+  RowStat* pstat = reinterpret_cast<RowStat*>(static_cast<char*>(ws) + kPartsHeader);
+  if (dtype == kBF16) {
+    EpiLogitsStats epi{};
+    epi.C = logits;
+    epi.ldc = V;
+    epi.M = M;
+    epi.N = V;
+    epi.typical = typical;
+    epi.inv_temp = inv_temp;
+    epi.ntiles = verify_tiles(M, V, H, dtype);
+    epi.header = header;
+    epi.pkey = pkey;
+    epi.pstat = pstat;
+    return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
+                       H, epi, st);
+  }
+  hipError_t e = run_lm_logits(x, M, H, LM, V, dtype, logits, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_parts_f32, dim3(M), dim3(256), 0, st, logits, M, V, typical, inv_temp,
+                     header, pkey, pstat);
+  return hipGetLastError();
 }
 
 }  // namespace medusa

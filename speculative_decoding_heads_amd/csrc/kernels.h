@@ -20,6 +20,16 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
                             void* u, int R, int base, hipStream_t st);
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
                          float* logits, hipStream_t st);
+// LM projection of the verify rows plus acceptance partials per (row, weight
+// tile) in ws: header (kPartsHeader bytes: ntiles, typical, rows), then
+// [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).
+constexpr size_t kPartsHeader = 256;
+int verify_tiles(int M, int N, int Kd, int dtype);
+// whether run_verify_logits leaves partials (else acceptance reads the logits)
+bool verify_uses_parts(int64_t M, int64_t N);
+size_t verify_workspace(int M, int N, int Kd, int dtype, int mode);
+hipError_t run_verify_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
+                             float* logits, int mode, float temperature, void* ws, hipStream_t st);
 
 // ---- top-k shortlists and root (topk.hip)
 struct TopkArgs {
@@ -90,7 +100,7 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
                       const int* depth, int b, int T, int V, int K, int mode, float temperature,
                       float eps, float delta, uint64_t seed, uint64_t step, int* L, int* path,
                       int* acc_tokens, int* bonus, void* ws, hipStream_t st,
-                      const KvRollback* kv = nullptr);
+                      const KvRollback* kv = nullptr, const void* parts = nullptr);
 
 // ---- compaction (compact.hip)
 hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,

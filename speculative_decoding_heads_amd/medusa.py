@@ -58,8 +58,10 @@ _SIGS = {
     "medusa_topk_tree": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _F, _U64, _U64,
                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P], _I32),
     "medusa_accept_compact": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _F, _F, _U64, _U64,
-                               _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P],
+                               _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P],
                               _I32),
+    "medusa_verify_workspace": ([_I64, _I32, _I32, _I32, _I32], _SZ),
+    "medusa_verify_logits": ([_P, _I64, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -328,7 +330,7 @@ def medusa_topk_tree(logits, k, kmax, N, decay_num, decay_den, root_mode, temper
 
 def medusa_accept_compact(base_logits, tokens, parent, depth, K, mode, temperature, eps, delta,
                           seed, step, L, path, acc_tokens, bonus, Kc, Vc, seq_len, ws,
-                          stream=None):
+                          verify_ws=None, stream=None):
     b, T, V = base_logits.shape
     _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus)
     _cache_shapes(Kc, Vc, seq_len, b)
@@ -336,6 +338,23 @@ def medusa_accept_compact(base_logits, tokens, parent, depth, K, mode, temperatu
     st = lib().medusa_accept_compact(_ptr(base_logits), _ptr(tokens), _ptr(parent), _ptr(depth), b,
                                      T, V, K, mode, temperature, eps, delta, seed, step, _ptr(L),
                                      _ptr(path), _ptr(acc_tokens), _ptr(bonus), _ptr(Kc), _ptr(Vc),
-                                     _ptr(seq_len), nkv, Pmax, d, dtype_code(Kc), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream))
+                                     _ptr(seq_len), nkv, Pmax, d, dtype_code(Kc), _ptr(verify_ws),
+                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check("medusa_accept_compact", st)
+
+
+def medusa_verify_workspace(rows, H, V, dtype, mode):
+    return lib().medusa_verify_workspace(rows, H, V, dtype, mode)
+
+
+def medusa_verify_logits(x, LM, logits, mode, temperature, ws, stream=None):
+    rows, H = x.shape
+    V = LM.shape[0]
+    _shape(LM, (V, H), "LM")
+    _dt(LM, x.dtype, "LM")
+    _need(logits.numel() == rows * V and logits.shape[-1] == V, "logits: expected rows*V entries")
+    _dt(logits, torch.float32, "logits")
+    st = lib().medusa_verify_logits(_ptr(x), rows, H, _ptr(LM), V, dtype_code(x), mode, temperature,
+                                    _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(stream))
+    _check("medusa_verify_logits", st)

@@ -12,8 +12,10 @@ accept and roll back); every part of the step runs in the HIP kernels.
     accept     : medusa_accept              -> L, path, acc_tokens, bonus
     rollback   : medusa_kv_compact          -> Kc, Vc, seq_len updated
 
-With ``fused=True`` (the default) shortlists + tree run as medusa_topk_tree and
-accept + rollback as medusa_accept_compact: the same outputs, two launches fewer.
+With ``fused=True`` (the default) shortlists + tree run as medusa_topk_tree, the
+verify logits as medusa_verify_logits (which also leaves the acceptance
+statistics per weight tile) and accept + rollback as medusa_accept_compact on
+those statistics: the same outputs, three launches fewer.
 """
 
 import torch
@@ -54,6 +56,8 @@ class VerifyStep:
         self.ws_attn = M.workspace(
             M.medusa_tree_attn_workspace(c.b, T, c.nq, c.nkv, c.d, c.Pmax, dt), device)
         self.ws_acc = M.workspace(M.medusa_accept_workspace(c.b, T), device)
+        self.ws_verify = M.workspace(
+            M.medusa_verify_workspace(c.b * T, c.nq * c.d, c.V, dt, self.mode), device)
 
     def run(self, x, step=0, stream=None, fused=True):
         """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len."""
@@ -73,14 +77,18 @@ class VerifyStep:
                                 self.depth, self.anc, stream=stream)
         M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], self.anc, self.O,
                            ws=self.ws_attn, stream=stream)
-        M.medusa_heads(self.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
-                       self.base_logits.view(c.b * c.T, c.V), include_base=1, stream=stream)
         if fused:
+            M.medusa_verify_logits(self.O.view(c.b * c.T, c.nq * c.d), x["LM"],
+                                   self.base_logits.view(c.b * c.T, c.V), self.mode,
+                                   c.temperature, self.ws_verify, stream=stream)
             M.medusa_accept_compact(self.base_logits, self.tokens, self.parent, self.depth, c.K,
                                     self.mode, c.temperature, c.eps, c.delta, c.seed, step, self.L,
                                     self.path, self.acc_tokens, self.bonus, x["Kc"], x["Vc"],
-                                    x["seq_len"], self.ws_acc, stream=stream)
+                                    x["seq_len"], self.ws_acc, verify_ws=self.ws_verify,
+                                    stream=stream)
         else:
+            M.medusa_heads(self.O.view(c.b * c.T, c.nq * c.d), None, x["LM"],
+                           self.base_logits.view(c.b * c.T, c.V), include_base=1, stream=stream)
             M.medusa_accept(self.base_logits, self.tokens, self.parent, self.depth, c.K, self.mode,
                             c.temperature, c.eps, c.delta, c.seed, step, self.L, self.path,
                             self.acc_tokens, self.bonus, self.ws_acc, stream=stream)

@@ -25,6 +25,12 @@ SMALL = [
     C.Config("fused_bf16_typical", 92, 2, 384, 5000, (5, 4, 3, 2), 60, 6, 3, 64, 700, "bf16",
              "typical"),
     C.LLAMA7B_BS1,
+    # rows * V >= 2^24: the verify GEMM leaves acceptance partials (ring kernel, greedy)
+    C.Config("fused_parts_ring", 93, 8, 128, 40000, (4, 4, 4), 64, 2, 1, 64, 200, "bf16", "greedy"),
+    # same with the tiled kernel (65 rows) and typical acceptance
+    C.Config("fused_parts_tiled", 94, 1, 128, 260000, (4, 4, 4), 64, 2, 2, 64, 300, "bf16",
+             "typical"),
+    C.LLAMA7B_BS16,
 ]
 
 OUTS = ("logits", "root", "idx", "val", "tokens", "pos", "parent", "depth", "anc", "O",
@@ -55,3 +61,25 @@ def test_fused_calls_match_separate_calls(cfg):
         assert torch.equal(ca[k], cb[k]), k
     # the rollback did run: seq_len = P + L + 1
     assert torch.equal(cb["seq_len"].cpu(), cfg.P + b["L"].cpu() + 1)
+
+
+@pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 3000), (5, 384, 31000),
+                                      (122, 384, 5000), (11, 256, 4096)])
+@pytest.mark.parametrize("mode", ["greedy", "typical"])
+def test_verify_logits_match_heads(rows, H, V, mode):
+    """medusa_verify_logits writes the same logits as medusa_heads (one kernel
+    choice for both), whatever it leaves in its workspace."""
+    from speculative_decoding_heads_amd import medusa as M
+    from speculative_decoding_heads_amd.synth import normal
+    say("verify logits", rows, H, V, mode)
+    dt = torch.float32 if rows == 11 else torch.bfloat16
+    x = normal((rows, H), rows + 7, 1.0, dt).to("cuda")
+    LM = normal((V, H), rows + 8, 0.02, dt).to("cuda")
+    a = torch.empty(rows, V, device="cuda")
+    b = torch.empty(rows, V, device="cuda")
+    M.medusa_heads(x, None, LM, a, include_base=1)
+    md = M.TYPICAL if mode == "typical" else M.GREEDY
+    ws = M.workspace(M.medusa_verify_workspace(rows, H, V, M.dtype_code(x), md))
+    M.medusa_verify_logits(x, LM, b, md, 0.7, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
