@@ -19,7 +19,9 @@
  *     allocates or frees device memory, synchronises, or copies device data
  *     to the host.  A failed launch returns MEDUSA_ERR_HIP.
  *   - Scratch memory is a caller-provided workspace `ws` of at least the
- *     size the matching *_workspace() query returns (host-only queries).
+ *     size the matching *_workspace() query returns (host-only queries),
+ *     16-byte aligned.  Its contents need no initialisation and are
+ *     overwritten by every call.
  *   - Floating-point inputs must be finite.  Values that only the device
  *     sees (token ids, seq_len, L, path) are range-checked by the kernels:
  *     an out-of-range seq_len gives NaN attention rows for that sequence and
@@ -105,8 +107,13 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
  *              exp((x_i - max x)/T) exceeds u * (the full sum), with
  *              u = (splitmix64(seed ^ step<<32 ^ s<<8 ^ 0) >> 40) * 2^-24
  *              for sequence s (SplitMix64: Steele, Lea, Flood 2014).
+ *              The sums are taken over 64 vocabulary slices and combined, so
+ *              a draw can differ from a serial float64 running sum only when
+ *              u * sum lies within rounding of a running sum.
  *   root   [b] i32; idx [b, K, kmax] i32 (descending; -1 past k_i);
  *   val    [b, K, kmax] f32 (the logits; -inf past k_i)
+ *   ws     medusa_topk_workspace bytes: the float64 sampler's per-slice
+ *          partial sums (64 slices per sequence).
  * ------------------------------------------------------------------------- */
 size_t medusa_topk_workspace(int32_t b, int32_t K, int32_t V, int32_t kmax);
 int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,

@@ -260,11 +260,14 @@ __global__ __launch_bounds__(1024) void accept_walk(const float* __restrict__ lo
   if (tid == 0 && ok) seq_len[s] = P + L + 1;
 }
 
-size_t accept_workspace(int b, int T) {
-  // amax / stats per node row, plus the chosen node per sequence
-  size_t rows = (size_t)b * T;
-  return rows * sizeof(RowStat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 64;
+// Workspace: stats per node row, amax per node row, the chosen node per
+// sequence, then (16-byte aligned) the sampler's slice partials.
+static size_t samp_offset(int b, int T) {
+  const size_t rows = (size_t)b * T;
+  return (rows * sizeof(RowStat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 15) & ~(size_t)15;
 }
+
+size_t accept_workspace(int b, int T) { return samp_offset(b, T) + sample_workspace(b); }
 
 hipError_t run_accept(const float* base_logits, const int* tokens, const int* parent,
                       const int* depth, int b, int T, int V, int K, int mode, float temperature,
@@ -305,7 +308,7 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,
-                         st);
+                         static_cast<char*>(ws) + samp_offset(b, T), st);
 }
 
 }  // namespace medusa

@@ -169,6 +169,7 @@ int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int3
   if ((int64_t)b * (K + 1) > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (K+1) > 65535");
   const size_t need = medusa_topk_workspace(b, K, V, kmax);
   if (need && (!ws || ws_bytes < need)) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
   TopkArgs a{};
   a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
   a.temperature = temperature; a.seed = seed; a.step = step;
@@ -263,6 +264,7 @@ int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const
   if ((int64_t)b * (K + 1) > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (K+1) > 65535");
   const size_t need = medusa_topk_workspace(b, K, V, kmax);
   if (need && (!ws || ws_bytes < need)) return fail(MEDUSA_ERR_WORKSPACE, "topk: workspace too small");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
   TopkArgs a{};
   a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
   a.temperature = temperature; a.seed = seed; a.step = step;
@@ -352,6 +354,7 @@ int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t
   if ((int64_t)b * T > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "b * T too large");
   const size_t need = medusa_accept_workspace(b, T);
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
   const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
   return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,
                                delta, seed, step, L, path, acc_tokens, bonus, ws,
@@ -389,6 +392,7 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
   if ((int64_t)b * T > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "b * T too large");
   const size_t need = medusa_accept_workspace(b, T);
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
   const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
   KvRollback kv{Kc, Vc, seq_len, nkv, Pmax, d, dtype};
   const void* parts = verify_ws && verify_uses_parts((int64_t)b * T, V) ? verify_ws : nullptr;

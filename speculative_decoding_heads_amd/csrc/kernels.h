@@ -65,9 +65,13 @@ hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx,
 // ---- sampling rows of softmax(x / T) in float64 (topk.hip)
 // Row of sequence s: base + s*seq_stride + (row_sel ? row_sel[s] : 0) * V.
 // The draw goes to out[s] and, if out2 is given, to out2[s * out2_stride].
+// ws: sample_workspace(b) bytes, 16-byte aligned (per-slice partial sums).
+constexpr int kSampSlices = 64;
+size_t sample_workspace(int b);
 hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
                            float temperature, uint64_t seed, uint64_t step, uint64_t draw,
-                           int* out, hipStream_t st, int* out2 = nullptr, int out2_stride = 0);
+                           int* out, void* ws, hipStream_t st, int* out2 = nullptr,
+                           int out2_stride = 0);
 
 hipError_t run_build_tree(const TreeDev& t, const int* root, const int* idx, int b,
                           const int* seq_len, int* tokens, int* pos, int* parent, int* depth,

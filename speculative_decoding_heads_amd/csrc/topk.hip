@@ -285,14 +285,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
   }
 }
 
+// The float64 sampler's slice partials (typical root draws).
 size_t topk_workspace(int b, int K, int V, int kmax) {
-  (void)b; (void)K; (void)V; (void)kmax;
-  return 0;
+  (void)K; (void)V; (void)kmax;
+  return sample_workspace(b);
 }
 
 hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
                     void* ws, hipStream_t st, const TreeDev* tree, const TreeOut* tree_out) {
-  (void)ws;
   const int rows = a.b * (a.K + 1);
   TreeDev t{};
   TreeOut o{};
@@ -306,74 +306,156 @@ hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx,
   if (e != hipSuccess) return e;
   if (a.root_mode == kTypical)
     return run_sample_rows(logits, (int64_t)(a.K + 1) * a.V, nullptr, a.b, a.V, a.temperature,
-                           a.seed, a.step, 0, root, st, tree ? o.tokens : nullptr,
+                           a.seed, a.step, 0, root, ws, st, tree ? o.tokens : nullptr,
                            tree ? t.T : 0);
   return hipSuccess;
 }
 
 // ---------------------------------------------------------------- sampling
-constexpr int kSampThreads = 1024;
+// Two launches per draw, so that a row's float64 exponentials spread over many
+// CUs:
+//   sample_part  - one workgroup per (row, slice): the row is cut into
+//                  kSampSlices contiguous slices; slice j yields its float
+//                  max m_j and s_j = sum exp((x_i - m_j) / T) in float64.
+//   sample_pick  - one workgroup per row: M = max m_j, c_j = s_j
+//                  exp((m_j - M) / T) (the slice's share of the row's sum
+//                  exp((x_i - M) / T)); the first slice whose running sum of
+//                  c exceeds u * sum c is rescanned element by element with
+//                  e_i = exp((x_i - M) / T), starting from the sum of the
+//                  slices before it.  The pick is the first element whose
+//                  running sum exceeds u * sum c; if rounding leaves none, the
+//                  slice's last element.
+// The running sums differ from a serial float64 sum only by rounding, so a
+// sample can differ from the serial rule only when u * sum lies within a few
+// ulps of a running sum.
+constexpr int kSampThreads = 256;
 
-__global__ __launch_bounds__(kSampThreads) void sample_rows(const float* __restrict__ base,
+struct SampPart {
+  double m;   // slice max (a float value), -inf for an empty slice
+  double s;   // sum of exp((x - m) / T) over the slice
+};
+
+__device__ __forceinline__ const float* samp_row(const float* base, int64_t seq_stride,
+                                                 const int* row_sel, int V, int s) {
+  const int rsel = row_sel ? row_sel[s] : 0;
+  return base + (int64_t)s * seq_stride + (int64_t)rsel * V;
+}
+
+__global__ __launch_bounds__(kSampThreads) void sample_part(const float* __restrict__ base,
                                                             int64_t seq_stride,
-                                                            const int* __restrict__ row_sel, int V,
-                                                            float temperature, uint64_t seed,
-                                                            uint64_t step, uint64_t draw,
+                                                            const int* __restrict__ row_sel,
+                                                            int V, float temperature,
+                                                            SampPart* __restrict__ parts) {
+  constexpr int NW = kSampThreads / 64;
+  const int j = blockIdx.x % kSampSlices, s = blockIdx.x / kSampSlices;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Ls = (V + kSampSlices - 1) / kSampSlices;
+  const int lo = min(V, j * Ls), hi = min(V, lo + Ls);
+  const float* x = samp_row(base, seq_stride, row_sel, V, s);
+  __shared__ float smax[NW];
+  __shared__ double ssum[NW];
+
+  float m = -INFINITY;
+  for (int e = lo + tid; e < hi; e += kSampThreads) m = fmaxf(m, x[e]);
+  m = wave_max(m);
+  if (lane == 0) smax[wave] = m;
+  __syncthreads();
+  m = smax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, smax[w]);
+  const double md = (double)m, td = (double)temperature;
+  double part = 0.0;
+  for (int e = lo + tid; e < hi; e += kSampThreads) part += exp(((double)x[e] - md) / td);
+  part = wave_sum_d(part);
+  if (lane == 0) ssum[wave] = part;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += ssum[w];
+    parts[(int64_t)s * kSampSlices + j] = SampPart{lo < hi ? md : -(double)INFINITY, t};
+  }
+}
+
+__global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restrict__ base,
+                                                            int64_t seq_stride,
+                                                            const int* __restrict__ row_sel,
+                                                            int V, float temperature,
+                                                            uint64_t seed, uint64_t step,
+                                                            uint64_t draw,
+                                                            const SampPart* __restrict__ parts,
                                                             int* __restrict__ out,
                                                             int* __restrict__ out2,
                                                             int out2_stride) {
+  static_assert(kSampSlices == 64, "one lane per slice");
+  constexpr int NW = kSampThreads / 64;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NW = kSampThreads / 64;
-  const int rsel = row_sel ? row_sel[s] : 0;
-  const float* x = base + (int64_t)s * seq_stride + (int64_t)rsel * V;
-  __shared__ float smax[NW];
-  __shared__ double ssum[NW];
-  __shared__ int found;
+  const int Ls = (V + kSampSlices - 1) / kSampSlices;
+  const float* x = samp_row(base, seq_stride, row_sel, V, s);
+  const double td = (double)temperature;
+  __shared__ int sh_j, found;
+  __shared__ double sh_base, sh_target, sh_max;
+  __shared__ double wsum[NW];
 
-  float m = -INFINITY;
-  for (int e = tid; e < V; e += kSampThreads) m = fmaxf(m, x[e]);
-  m = wave_max(m);
-  if (lane == 0) smax[wave] = m;
-  if (tid == 0) found = V - 1;
+  if (wave == 0) {
+    const SampPart p = parts[(int64_t)s * kSampSlices + lane];
+    const double M = (double)wave_max((float)p.m);
+    const double c = p.m == -(double)INFINITY ? 0.0 : p.s * exp((p.m - M) / td);
+    double incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const double total = __shfl(incl, 63, 64);
+    const double prev = __shfl_up(incl, 1, 64);
+    const double excl = lane > 0 ? prev : 0.0;
+    const double target = counter_uniform(seed, step, (uint64_t)s, draw) * total;
+    const uint64_t over = __ballot(incl > target);
+    const uint64_t live = __ballot(c > 0.0);
+    // the first slice whose running sum passes the target; if rounding
+    // leaves none, the last slice with any mass
+    const int js = over ? __ffsll((long long)over) - 1
+                        : (live ? 63 - __clzll((long long)live) : 0);
+    if (lane == js) {
+      sh_j = js;
+      sh_base = excl;
+      sh_target = target;
+      sh_max = M;
+    }
+    if (lane == 0) found = -1;
+  }
   __syncthreads();
-  m = smax[0];
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, smax[w]);
-
-  const double md = (double)m, td = (double)temperature;
-  const int chunk = (V + kSampThreads - 1) / kSampThreads;
-  const int lo = min(V, tid * chunk), hi = min(V, lo + chunk);
+  const int j = sh_j;
+  const double b0 = sh_base, target = sh_target, md = sh_max;
+  const int lo = min(V, j * Ls), hi = min(V, lo + Ls);
+  // contiguous pieces of the slice in thread order = vocabulary order
+  const int per = (hi - lo + kSampThreads - 1) / kSampThreads;
+  const int tlo = min(hi, lo + tid * per), thi = min(hi, tlo + per);
   double part = 0.0;
-  for (int e = lo; e < hi; ++e) part += exp(((double)x[e] - md) / td);
-
-  // block exclusive scan of the slice sums (thread order = vocabulary order)
+  for (int e = tlo; e < thi; ++e) part += exp(((double)x[e] - md) / td);
   double incl = part;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    double y = __shfl_up(incl, o, 64);
+    const double y = __shfl_up(incl, o, 64);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) ssum[wave] = incl;
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  // Slice bounds are built so that thread t's end equals thread t+1's start
-  // bit for bit (same additions in the same order); exactly one slice holds
-  // the crossing.
-  double wpre = 0.0, total = 0.0;
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) wpre = wpre + ssum[w];
-    total = total + ssum[w];
-  }
-  const double prev_incl = __shfl_up(incl, 1, 64);
-  const double excl = wpre + (lane > 0 ? prev_incl : 0.0);
-  const double end = wpre + incl;
-  const double u = counter_uniform(seed, step, (uint64_t)s, draw);
-  const double target = u * total;
-  if (excl <= target && end > target) {
-    double run = 0.0;
-    int pick = hi - 1;
-    for (int e = lo; e < hi; ++e) {
+  // thread t's end and thread t+1's start come from the same additions, so
+  // they are equal bit for bit and at most one thread brackets the target
+  double wpre = 0.0;
+  for (int w = 0; w < wave; ++w) wpre = wpre + wsum[w];
+  const double prev = __shfl_up(incl, 1, 64);
+  const double start = b0 + (wpre + (lane > 0 ? prev : 0.0));
+  const double end = b0 + (wpre + incl);
+  if (tlo < thi && start <= target && end > target) {
+    double run = start;
+    int pick = thi - 1;
+    for (int e = tlo; e < thi; ++e) {
       run += exp(((double)x[e] - md) / td);
-      if (excl + run > target) {
+      if (run > target) {
         pick = e;
         break;
       }
@@ -382,16 +464,22 @@ __global__ __launch_bounds__(kSampThreads) void sample_rows(const float* __restr
   }
   __syncthreads();
   if (tid == 0) {
-    out[s] = found;
-    if (out2) out2[(int64_t)s * out2_stride] = found;
+    const int pick = found >= 0 ? found : max(lo, hi - 1);
+    out[s] = pick;
+    if (out2) out2[(int64_t)s * out2_stride] = pick;
   }
 }
 
+size_t sample_workspace(int b) { return (size_t)b * kSampSlices * sizeof(SampPart); }
+
 hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
-                           float temperature, uint64_t seed, uint64_t step, uint64_t draw,
-                           int* out, hipStream_t st, int* out2, int out2_stride) {
-  hipLaunchKernelGGL(sample_rows, dim3(b), dim3(kSampThreads), 0, st, base, seq_stride, row_sel, V,
-                     temperature, seed, step, draw, out, out2, out2_stride);
+                           float temperature, uint64_t seed, uint64_t step, uint64_t draw, int* out,
+                           void* ws, hipStream_t st, int* out2, int out2_stride) {
+  SampPart* parts = static_cast<SampPart*>(ws);
+  hipLaunchKernelGGL(sample_part, dim3((unsigned)b * kSampSlices), dim3(kSampThreads), 0, st, base,
+                     seq_stride, row_sel, V, temperature, parts);
+  hipLaunchKernelGGL(sample_pick, dim3(b), dim3(kSampThreads), 0, st, base, seq_stride, row_sel, V,
+                     temperature, seed, step, draw, parts, out, out2, out2_stride);
   return hipGetLastError();
 }
 

@@ -127,8 +127,9 @@ def test_validation_before_launch():
 def test_workspace_queries_are_host_only_and_sized():
     assert M.medusa_heads_workspace(1, 4096, 4, 1, M.BF16) >= 5 * 4096 * 2
     assert M.medusa_heads_workspace(65, 4096, 0, 1, M.BF16) == 0
-    assert M.medusa_topk_workspace(16, 4, 32000, 10) == 0      # top-k needs no scratch
-    assert M.medusa_accept_workspace(16, 65) >= 16 * 65 * 16
+    # the float64 sampler keeps 64 slice partials (16 bytes each) per sequence
+    assert M.medusa_topk_workspace(16, 4, 32000, 10) >= 16 * 64 * 16
+    assert M.medusa_accept_workspace(16, 65) >= 16 * 65 * 16 + 16 * 64 * 16
     # the 7B batch-1 attention splits the prefix; the long-context batch-32 one does not
     assert M.medusa_tree_attn_workspace(1, 65, 32, 32, 128, 2048 + 65, M.BF16) > 0
     assert M.medusa_tree_attn_workspace(1, 11, 4, 4, 64, 139, M.F32) == 0

@@ -160,6 +160,26 @@ def test_topk_typical_root_is_counter_sample():
         assert list(idx[s, 0]) == list(topk_stable(x[s, 1], 3))
 
 
+@pytest.mark.parametrize("V,scale", [(1, 1.0), (7, 3.0), (63, 1.0), (64, 2.0), (65, 0.5),
+                                     (100, 30.0), (4097, 1.0), (32000, 0.05), (128256, 4.0)])
+def test_typical_root_samples_across_vocab_sizes(V, scale):
+    """The sampler cuts a row into 64 slices (empty ones when V < 64): many
+    draws, flat to peaked rows, against the serial float64 rule."""
+    b = 48
+    logits = normal((b, 2, V), V + 5, scale, torch.float32)
+    T = float(np.float32(0.7))
+    root, _, _ = _topk_run(logits, (1,), 1, M.TYPICAL, temperature=T, seed=0xABC, step=V)
+    x = logits.numpy()
+    compared = 0
+    for s in range(b):
+        u = counter_uniform(0xABC, V, s, 0)
+        want, c = sample_tempered(x[s, 0], T, u)
+        if np.min(np.abs(c - u * c[-1])) / c[-1] > 1e-12:
+            assert root[s] == want, (s, int(root[s]), want)
+            compared += 1
+    assert compared >= b - 2
+
+
 # ------------------------------------------------------------------ tree
 @pytest.mark.parametrize("k,N,b", [((2, 2, 1), None, 1), ((10,) * 4, 64, 3), ((10,) * 5, 128, 2),
                                    ((3, 2), 5, 1), ((16, 16), 255, 2), ((4,), 0, 2)])
