@@ -21,6 +21,8 @@
 //     online (m, s, t) with s = sum e^(x'-m), t = sum e^(x'-m)(x'-m),
 //     x' = x / T, rescaled whenever the running max moves; then
 //     H = ln s - t/s and log q(tok) = x'_tok - m - ln s.
+//   accept_parts: the same statistics merged from the verify GEMM's per-tile
+//     partials, one wave per node row.
 //   accept_walk: one workgroup per sequence: local flags, full-path flags by
 //     walking ancestors, block max/min for L and the chosen node, path and
 //     accepted tokens.
@@ -105,6 +107,50 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __rest
   }
 }
 
+// The same statistics from the verify GEMM's per-tile partials: one wave per
+// node row; each lane merges tiles lane, lane + 64, ... (four in flight), then
+// the wave reduces its lanes.
+template <int MODE>
+__global__ __launch_bounds__(256) void accept_parts(const int* __restrict__ hdr,
+                                                    const uint64_t* __restrict__ pkey,
+                                                    const RowStat* __restrict__ pstat, int rows,
+                                                    int* __restrict__ amax,
+                                                    RowStat* __restrict__ stats) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int ntiles = hdr[0];
+  RowPart acc;
+  part_init(acc);
+  for (int j0 = 0; j0 < ntiles; j0 += 4 * 64) {
+    RowPart q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * 64 + lane;
+      const int64_t o = (int64_t)row * ntiles + min(j, ntiles - 1);
+      const bool ok = j < ntiles;
+      if (MODE == kGreedy) {
+        q[u].key = ok ? pkey[o] : 0ull;
+      } else {
+        const RowStat st = pstat[o];
+        q[u].m = st.m;
+        q[u].s = ok ? st.s : 0.f;
+        q[u].t = st.t;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) part_merge(acc, q[u], MODE == kTypical);
+  }
+  if (MODE == kGreedy) {
+    acc.key = wave_max_u64(acc.key);
+    if (lane == 0) amax[row] = (int)key_index(acc.key);
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part_xor(acc, o, true);
+    if (lane == 0) stats[row] = RowStat{acc.m, acc.s, acc.t, 0.f};
+  }
+}
+
 __device__ __forceinline__ bool full_path(int c, const int* sparent, const unsigned char* local) {
   bool full = true;
   for (int a = c; a > 0;) {
@@ -117,7 +163,7 @@ __device__ __forceinline__ bool full_path(int c, const int* sparent, const unsig
 }
 
 template <int MODE>
-__global__ __launch_bounds__(1024) void accept_walk(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ logits,
                                                    const int* __restrict__ tokens,
                                                    const int* __restrict__ parent,
                                                    const int* __restrict__ depth, int T, int V,
@@ -129,98 +175,56 @@ __global__ __launch_bounds__(1024) void accept_walk(const float* __restrict__ lo
                                                    int* __restrict__ bonus, int* __restrict__ best_out,
                                                    uint8_t* __restrict__ Kc, uint8_t* __restrict__ Vc,
                                                    int* __restrict__ seq_len, int nkv, int Pmax,
-                                                   int row_bytes, const int* __restrict__ parts_hdr,
-                                                   const uint64_t* __restrict__ pkey,
-                                                   const RowStat* __restrict__ pstat) {
+                                                   int row_bytes) {
   const int s = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   __shared__ int spath[kMaxHeads + 1];
   const int P = Kc ? seq_len[s] : 0;
   __shared__ unsigned char local[kMaxT];
   __shared__ int sdepth[kMaxT], sparent[kMaxT];
   __shared__ int samax[kMaxT];
   __shared__ RowStat sstat[kMaxT];
+  __shared__ int stok[kMaxT];
   __shared__ int bestL, bestNode;
   if (tid == 0) { bestL = 0; bestNode = 0x7fffffff; }
-  // per-node statistics of this sequence: from the verify GEMM's partials
-  // (one wave per node row, lanes over the weight tiles), or per row as given
-  if (parts_hdr) {
-    const int ntiles = parts_hdr[0];
-    const int nw = blockDim.x / 64;
-    // four rows of a wave at a time, four tiles per lane and row in flight
-    constexpr int RR = 4;
-    for (int p0 = wave; p0 < T; p0 += RR * nw) {
-      RowPart acc2[RR];
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) part_init(acc2[rr]);
-      for (int j0 = 0; j0 < ntiles; j0 += 4 * 64) {
-        RowPart q[RR][4];
-#pragma unroll
-        for (int rr = 0; rr < RR; ++rr)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = min(p0 + rr * nw, T - 1), j = j0 + u * 64 + lane;
-            const int64_t o = ((int64_t)s * T + p) * ntiles + min(j, ntiles - 1);
-            const bool ok = j < ntiles;
-            if (MODE == kGreedy) {
-              q[rr][u].key = ok ? pkey[o] : 0ull;
-            } else {
-              const RowStat st = pstat[o];
-              q[rr][u].m = st.m;
-              q[rr][u].s = ok ? st.s : 0.f;
-              q[rr][u].t = st.t;
-            }
-          }
-#pragma unroll
-        for (int rr = 0; rr < RR; ++rr)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) part_merge(acc2[rr], q[rr][u], MODE == kTypical);
-      }
-#pragma unroll
-      for (int rr = 0; rr < RR; ++rr) {
-        if (MODE == kGreedy) {
-          acc2[rr].key = wave_max_u64(acc2[rr].key);
-        } else {
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) part_xor(acc2[rr], o, true);
-        }
-        const int p = p0 + rr * nw;
-        if (lane == 0 && p < T) {
-          samax[p] = (int)key_index(acc2[rr].key);
-          sstat[p] = RowStat{acc2[rr].m, acc2[rr].s, acc2[rr].t, 0.f};
-        }
-      }
-    }
-  } else {
-    for (int p = tid; p < T; p += blockDim.x) {
-      const int64_t row = (int64_t)s * T + p;
-      if (MODE == kGreedy) samax[p] = amax[row];
-      else sstat[p] = stats[row];
-    }
+  // Node c (thread c; T <= kMaxT <= blockDim.x): its parent, depth, token and
+  // (typical) the logit of its token in the parent's row are loaded before the
+  // statistics below, so their latency overlaps that work.
+  int my_parent = -1, my_tok = -1;
+  bool my_valid = false;
+  float my_logit = 0.f;
+  if (tid < T) {
+    my_parent = parent[tid];
+    my_tok = tokens[(int64_t)s * T + tid];
+    sparent[tid] = my_parent;
+    sdepth[tid] = depth[tid];
+    stok[tid] = my_tok;
+    my_valid = tid > 0 && my_tok >= 0 && my_tok < V && my_parent >= 0 && my_parent < tid;
+    if (MODE == kTypical && my_valid)
+      my_logit = logits[((int64_t)s * T + my_parent) * V + my_tok];
+  }
+  // per-node statistics of this sequence
+  for (int p = tid; p < T; p += blockDim.x) {
+    const int64_t row = (int64_t)s * T + p;
+    if (MODE == kGreedy) samax[p] = amax[row];
+    else sstat[p] = stats[row];
   }
   __syncthreads();
-  for (int c = tid; c < T; c += blockDim.x) {
-    sparent[c] = parent[c];
-    sdepth[c] = depth[c];
-    bool ok = (c == 0);
-    if (c > 0) {
-      const int p = parent[c];
-      const int tok = tokens[(int64_t)s * T + c];
-      const int64_t prow = (int64_t)s * T + p;
-      if (tok >= 0 && tok < V && p >= 0 && p < c) {
-        if (MODE == kGreedy) {
-          ok = tok == samax[p];
-        } else {
-          const RowStat st = sstat[p];
-          const double lns = log((double)st.s);
-          const double H = lns - (double)st.t / (double)st.s;
-          const double logq = (double)(logits[prow * V + tok] * inv_temp) - (double)st.m - lns;
-          const double thr = fmin((double)eps, (double)delta * exp(-H));
-          ok = exp(logq) > thr;
-        }
+  if (tid < T) {
+    bool ok = tid == 0;
+    if (my_valid) {
+      if (MODE == kGreedy) {
+        ok = my_tok == samax[my_parent];
+      } else {
+        const RowStat st = sstat[my_parent];
+        const double lns = log((double)st.s);
+        const double H = lns - (double)st.t / (double)st.s;
+        const double logq = (double)(my_logit * inv_temp) - (double)st.m - lns;
+        const double thr = fmin((double)eps, (double)delta * exp(-H));
+        ok = exp(logq) > thr;
       }
     }
-    local[c] = ok;
+    local[tid] = ok;
   }
   __syncthreads();
   // A parent table is valid when 0 <= parent[c] < c; anything else is treated
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(1024) void accept_walk(const float* __restrict__ lo
     for (int d = L; d >= 0; --d) {
       path[(int64_t)s * (K + 1) + d] = a;
       spath[d] = a;
-      acc_tokens[(int64_t)s * (K + 1) + d] = tokens[(int64_t)s * T + a];
+      acc_tokens[(int64_t)s * (K + 1) + d] = stok[a];
       a = a > 0 ? sparent[a] : 0;
     }
     if (MODE == kGreedy) bonus[s] = samax[best];
@@ -289,22 +293,28 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
       parts ? reinterpret_cast<const uint64_t*>(static_cast<const char*>(parts) + kPartsHeader) : nullptr;
   const RowStat* pstat =
       parts ? reinterpret_cast<const RowStat*>(static_cast<const char*>(parts) + kPartsHeader) : nullptr;
+  const unsigned pgrid = (unsigned)((rows + 3) / 4);
   if (mode == kGreedy) {
-    if (!parts)
+    if (parts)
+      hipLaunchKernelGGL(accept_parts<kGreedy>, dim3(pgrid), dim3(256), 0, st, hdr, pkey, pstat,
+                         (int)rows, amax, stats);
+    else
       hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
                          base_logits, V, inv_temp, amax, stats);
-    hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(parts ? 1024 : 256), 0, st, base_logits, tokens,
+    hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
                        parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
-                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, hdr, pkey,
-                       pstat);
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
     return hipGetLastError();
   }
-  if (!parts)
+  if (parts)
+    hipLaunchKernelGGL(accept_parts<kTypical>, dim3(pgrid), dim3(256), 0, st, hdr, pkey, pstat,
+                       (int)rows, amax, stats);
+  else
     hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
                        base_logits, V, inv_temp, amax, stats);
-  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(parts ? 1024 : 256), 0, st, base_logits, tokens, parent,
+  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
                      depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,
-                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, hdr, pkey, pstat);
+                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,

@@ -6,13 +6,13 @@
 //
 // Selection is one launch, one workgroup per row (see topk_rows).
 // The root row (head 0) takes k = 1 in greedy mode; in typical mode the root
-// is drawn by sample_rows instead.
+// is drawn by the row sampler instead.
 //
-// sample_rows draws from softmax(x / T) in float64: e_i = exp((x_i - max)/T),
-// the smallest i whose running sum (vocabulary order) exceeds u * sum e, with
-// u from the SplitMix64 counter.  Each thread owns one contiguous slice; slice
-// sums are scanned across the block, and the slice holding the crossing is
-// rescanned serially.
+// The row sampler (run_sample_rows) draws from softmax(x / T) in float64:
+// e_i = exp((x_i - max)/T), the smallest i whose running sum (vocabulary
+// order) exceeds u * sum e, with u from the SplitMix64 counter.  Slice sums
+// come from many workgroups (sample_part); one workgroup per row then finds
+// the slice holding the crossing and rescans it (sample_pick).
 
 #include "common.h"
 #include "kernels.h"
@@ -316,7 +316,8 @@ hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx,
 // CUs:
 //   sample_part  - one workgroup per (row, slice): the row is cut into
 //                  kSampSlices contiguous slices; slice j yields its float
-//                  max m_j and s_j = sum exp((x_i - m_j) / T) in float64.
+//                  max m_j and s_j = sum exp((x_i - m_j) / T) in float64
+//                  (the division taken as a product with 1/T).
 //   sample_pick  - one workgroup per row: M = max m_j, c_j = s_j
 //                  exp((m_j - M) / T) (the slice's share of the row's sum
 //                  exp((x_i - M) / T)); the first slice whose running sum of
@@ -363,9 +364,9 @@ __global__ __launch_bounds__(kSampThreads) void sample_part(const float* __restr
   m = smax[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) m = fmaxf(m, smax[w]);
-  const double md = (double)m, td = (double)temperature;
+  const double md = (double)m, rt = 1.0 / (double)temperature;
   double part = 0.0;
-  for (int e = lo + tid; e < hi; e += kSampThreads) part += exp(((double)x[e] - md) / td);
+  for (int e = lo + tid; e < hi; e += kSampThreads) part += exp(((double)x[e] - md) * rt);
   part = wave_sum_d(part);
   if (lane == 0) ssum[wave] = part;
   __syncthreads();
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Ls = (V + kSampSlices - 1) / kSampSlices;
   const float* x = samp_row(base, seq_stride, row_sel, V, s);
-  const double td = (double)temperature;
+  const double rt = 1.0 / (double)temperature;
   __shared__ int sh_j, found;
   __shared__ double sh_base, sh_target, sh_max;
   __shared__ double wsum[NW];
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   if (wave == 0) {
     const SampPart p = parts[(int64_t)s * kSampSlices + lane];
     const double M = (double)wave_max((float)p.m);
-    const double c = p.m == -(double)INFINITY ? 0.0 : p.s * exp((p.m - M) / td);
+    const double c = p.m == -(double)INFINITY ? 0.0 : p.s * exp((p.m - M) * rt);
     double incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   const int per = (hi - lo + kSampThreads - 1) / kSampThreads;
   const int tlo = min(hi, lo + tid * per), thi = min(hi, tlo + per);
   double part = 0.0;
-  for (int e = tlo; e < thi; ++e) part += exp(((double)x[e] - md) / td);
+  for (int e = tlo; e < thi; ++e) part += exp(((double)x[e] - md) * rt);
   double incl = part;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
     double run = start;
     int pick = thi - 1;
     for (int e = tlo; e < thi; ++e) {
-      run += exp(((double)x[e] - md) / td);
+      run += exp(((double)x[e] - md) * rt);
       if (run > target) {
         pick = e;
         break;
