@@ -41,16 +41,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f3
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// v_mfma_f32_32x32x16_bf16.  Lane l supplies A[l%32][slot 8*(l/32)+j] and
-// B[slot 8*(l/32)+j][l%32], j = 0..7, and receives
-// D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator r = 0..15 (checked by an
-// in-bounds probe against a CPU product).
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-__device__ __forceinline__ f32x16 mfma32x32x16(const uint4& a, const uint4& b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
 // ---- loads ----------------------------------------------------------------------
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 // Streaming (single-use) load: non-temporal hint so it does not evict reused lines.

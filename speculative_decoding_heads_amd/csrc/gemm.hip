@@ -527,179 +527,6 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   }
 }
 
-// ---------------------------------------------------------------- MFMA-bound, 32x32 blocks
-// The same ring of 32-wide K slices, with v_mfma_f32_32x32x16_bf16: a 32x32
-// block needs two 16-byte fragments per 16 K where the 16x16 instruction needs
-// two per 16x16 block, so LDS reads per flop halve for the same register tile.
-// Four waves, 2 (M) x 2 (N), one per SIMD, each owning WMB x WNB blocks:
-// tile BM = 64*WMB activation rows x BN = 64*WNB weight rows.  With 4 x 4
-// blocks the accumulators take 256 registers per lane (the accumulation
-// registers of a wave that has its SIMD to itself).
-template <int WMB, int WNB, class Epi>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_mf32_bf16(const uint16_t* __restrict__ X, int64_t ldx, int M,
-                    const uint16_t* __restrict__ W, int N, int Kd, int ntm, Epi epi) {
-  constexpr int NW = 4;
-  constexpr int BM = 64 * WMB, BN = 64 * WNB, BK = 32, NS = 4;
-  constexpr int XR = BM / 16, WR = BN / 16;          // 1 KB regions per slice
-  constexpr int XPW = (XR + NW - 1) / NW, WPW = (WR + NW - 1) / NW;
-  constexpr int D = XPW + WPW;                       // DMA issues per wave per slice
-  __shared__ __attribute__((aligned(16))) uint16_t xs[NS][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t wsm[NS][BN * BK];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r32 = lane & 31, h = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int tm = t % ntm, tn = t / ntm;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = Kd / BK;
-
-  const uint16_t* xsrc[XPW];
-  const uint16_t* wsrc[WPW];
-  uint32_t xoff[XPW], woff[WPW];
-#pragma unroll
-  for (int j = 0; j < XPW; ++j) {
-    const int r = min(wave + NW * j, XR - 1);
-    const int row = 16 * r + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
-    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch;
-    xoff[j] = (uint32_t)(r * 1024);
-  }
-#pragma unroll
-  for (int j = 0; j < WPW; ++j) {
-    const int r = min(wave + NW * j, WR - 1);
-    const int row = 16 * r + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
-    wsrc[j] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ch;
-    woff[j] = (uint32_t)(r * 1024);
-  }
-  const uint32_t xl = lds_u32(&xs[0][0]), wl = lds_u32(&wsm[0][0]);
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < XPW; ++j)
-      dma16(xsrc[j] + k0, __builtin_amdgcn_readfirstlane(xl + (uint32_t)(buf * BM * BK * 2) + xoff[j]));
-#pragma unroll
-    for (int j = 0; j < WPW; ++j)
-      dma16(wsrc[j] + k0, __builtin_amdgcn_readfirstlane(wl + (uint32_t)(buf * BN * BK * 2) + woff[j]));
-  };
-
-  f32x16 acc[WNB][WMB];
-#pragma unroll
-  for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nb][mb][i] = 0.f;
-
-  // Slice rows are 64 bytes = four 16-byte chunks, chunk c of row r stored at
-  // c ^ ((r >> 2) & 3); 16-K step ks reads chunk 2*ks + (lane >> 5).
-  // Fragment reads run one 16-K step ahead of the MFMAs (the second step's
-  // fragments load during the first step's MFMAs, the next slice's first step
-  // during the second), so a wave that has its SIMD alone rarely waits on LDS.
-  uint4 f0a[WNB], f0b[WMB], f1a[WNB], f1b[WMB];
-  auto rd = [&](int buf, int ks, uint4 (&a)[WNB], uint4 (&b)[WMB]) {
-    const int c = 2 * ks + h;
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      const int row = wn * 32 * WNB + 32 * nb + r32;
-      a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * (c ^ ((row >> 2) & 3))]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) {
-      const int row = wm * 32 * WMB + 32 * mb + r32;
-      b[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * (c ^ ((row >> 2) & 3))]);
-    }
-  };
-  auto mm = [&](const uint4 (&a)[WNB], const uint4 (&b)[WMB]) {
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < WMB; ++mb) acc[nb][mb] = mfma32x32x16(a[nb], b[mb], acc[nb][mb]);
-  };
-
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (i < nk) issue(i, i);
-  {
-    const int ahead = min(NS - 2, nk - 1);
-    if (ahead >= 2) vm_wait<2 * D>();
-    else if (ahead == 1) vm_wait<D>();
-    else vm_wait<0>();
-  }
-  __syncthreads();
-  if (NS - 1 < nk) issue(NS - 1, NS - 1);
-  rd(0, 0, f0a, f0b);
-  for (int kt = 0; kt < nk; ++kt) {
-    // the step-0 fragments were read a step of MFMAs ago: waiting for them
-    // here is free and tells the compiler that the MFMAs below need not wait
-    // for the reads issued next (lgkmcnt(0), other counters unconstrained)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    rd(kt % NS, 1, f1a, f1b);
-    __builtin_amdgcn_sched_barrier(0);
-    mm(f0a, f0b);
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      // slice kt+1 landed (this wave's DMA; later slices may stay in flight);
-      // the barrier makes it visible and frees slice kt's buffer (every wave
-      // has its fragments in registers).  After the last slice the same steps
-      // run on a stale buffer whose fragments go unused: one straight path
-      // keeps the compiler's LDS wait bookkeeping exact.
-      const int ahead = min(2, nk - 2 - kt);
-      if (ahead >= 2) vm_wait<2 * D>();
-      else if (ahead == 1) vm_wait<D>();
-      else vm_wait<0>();
-      __syncthreads();
-      if (kt + NS < nk) issue(kt + NS, (kt + NS) % NS);
-      rd((kt + 1) % NS, 0, f0a, f0b);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mm(f1a, f1b);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // lane: activation row m (lane & 31), weight rows 8q + 4(lane >> 5) + 0..3
-#pragma unroll
-  for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        epi.store4(m0 + wm * 32 * WMB + 32 * mb + r32, n0 + wn * 32 * WNB + 32 * nb + 8 * q + 4 * h,
-                   f32x4{acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
-                         acc[nb][mb][4 * q + 3]});
-  if constexpr (HasParts<Epi>::value) {
-    // row partials over this workgroup's BN columns: a lane's 16*WNB values,
-    // the lane pair of a row (lanes l, l + 32), then the two waves along N
-    __syncthreads();                        // every wave is past its last read of xs
-    RowPart* red = reinterpret_cast<RowPart*>(&xs[0][0]);
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) {
-      float v[16 * WNB];
-      int col[16 * WNB];
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          v[16 * nb + i] = acc[nb][mb][i];
-          col[16 * nb + i] = n0 + wn * 32 * WNB + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
-        }
-      RowPart pt = lane_part(v, col, N, epi.typical, epi.inv_temp);
-      part_xor(pt, 32, epi.typical);
-      if (h == 0) red[wn * BM + wm * 32 * WMB + 32 * mb + r32] = pt;
-    }
-    __syncthreads();
-    for (int r = threadIdx.x; r < BM; r += 256) {
-      if (m0 + r >= M) continue;
-      RowPart pt = red[r];
-      part_merge(pt, red[BM + r], epi.typical);
-      epi.write_part(m0 + r, tn, pt);
-    }
-    epi.write_header();
-  }
-}
-
 // ---------------------------------------------------------------- f32
 // One wave per weight row n; lanes split K; M <= 64 rows, looped in groups of 8.
 template <class Epi>
