@@ -204,6 +204,40 @@ def copy_calibration(mib):
     del src, dst
 
 
+def measured_peaks(log=print):
+    """Achievable reference rates on this GPU, reported next to the spec-sheet
+    peaks: a 1 GiB device copy (read + write bytes), a 1 GiB reduction (read
+    bytes) and a vendor bf16 GEMM (8192 x 8192 x 8192, library call).  These
+    use torch/library kernels only as yardsticks; no part of the step does."""
+    import torch
+    def timed(fn, iters):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / iters * 1e-3
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    words = src.view(torch.float32)
+    t_read = timed(lambda: words.sum(), 10)
+    del src, dst, words
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, b), 10)
+    out = {"copy_GBps": round(2 * n / t_copy / 1e9, 1), "read_GBps": round(n / t_read / 1e9, 1),
+           "vendor_bf16_gemm_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
+           "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_TFLOPs": BF16_PEAK_TFLOPS}
+    log(f"measured peaks: {out}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +249,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy / read / vendor-GEMM reference rates")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +309,7 @@ def main():
                        "step_effective_GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
                        "per_call_us": {k: round(v, 2) for k, v in pc2.items()}}
     torch.cuda.synchronize()
+    out["measured_peaks"] = None if args.no_peaks else measured_peaks(log)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds, log)
     print(json.dumps(out), flush=True)
 
