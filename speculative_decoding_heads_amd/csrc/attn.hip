@@ -129,12 +129,18 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   const int64_t kvbase = ((int64_t)b * nkv + g) * (int64_t)Pmax * D;
 
   // DMA issue j of this thread fills 1 KB region j*8 + wave of a tile: rows
-  // ROWS_KB*region + lane/CPR, LDS chunk lane%CPR <- global chunk (lane%CPR) ^ (row & SWZ).
+  // ROWS_KB*region + lane/CPR, LDS chunk lane%CPR <- global chunk
+  // (lane%CPR) ^ swz(row).  With 16 chunks per row swz(row) = (row & 7) << 1
+  // (chunk bit 0 free): the K fragment reads pair neighbouring chunks of one
+  // row (lanes 16 apart) and the transposing V reads neighbouring chunks of
+  // four rows, and both then land on distinct banks (row & 15 made them
+  // collide).
+  auto swz = [](int row) { return CPR == 16 ? ((row & 7) << 1) : (row & SWZ); };
   int drow[NI], dcol[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     drow[j] = (j * kWaves + wave) * ROWS_KB + lane / CPR;
-    dcol[j] = 8 * ((lane % CPR) ^ (drow[j] & SWZ));
+    dcol[j] = 8 * ((lane % CPR) ^ swz(drow[j]));
   }
   const uint32_t klds = lds_u32(&kbuf[0][0]), vlds = lds_u32(&vbuf[0][0]);
   auto issue = [&](int tile, int buf) {
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
         const int krow = 32 * ks + 16 * h + r16;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(kb_ + krow * D + 8 * ((4 * ds + g4) ^ (krow & SWZ)));
+          const uint4 kf = *reinterpret_cast<const uint4*>(kb_ + krow * D + 8 * ((4 * ds + g4) ^ swz(krow)));
 #pragma unroll
           for (int rb = 0; rb < NV; ++rb) s[rb][h] = mfma16x16x32(kf, qf[rb][ds], s[rb][h]);
         }
@@ -268,8 +274,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
       for (int db = 0; db < DB; ++db) {
         const int cb = 32 * db + 8 * (r16 & 3);
         const int ch = cb >> 4, he = (cb & 15) >> 1;
-        const uint2 lo = lds_read_tr16(vb_ + vrow * D + 8 * (ch ^ (vrow & SWZ)) + he);
-        const uint2 hi = lds_read_tr16(vb_ + (vrow + 16) * D + 8 * (ch ^ ((vrow + 16) & SWZ)) + he);
+        const uint2 lo = lds_read_tr16(vb_ + vrow * D + 8 * (ch ^ swz(vrow)) + he);
+        const uint2 hi = lds_read_tr16(vb_ + (vrow + 16) * D + 8 * (ch ^ swz(vrow + 16)) + he);
         uint4 va;
         va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
 #pragma unroll

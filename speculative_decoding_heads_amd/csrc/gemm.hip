@@ -259,7 +259,12 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
   constexpr int NT = 64 * NWAVES;
   constexpr int BM = 16 * MB;
   constexpr int BN = 16 * NBW * NWAVES;
-  constexpr int LDSROW = 128 + 8;              // bf16 elements per LDS row (16 B pad)
+  constexpr int LDSROW = 128;                  // bf16 elements per LDS row
+  // The 16 chunks (16 B) of an activation row are XOR-swizzled by
+  // (r & 3) | ((r & 4) << 1): a fragment read has lanes 16 apart read chunks 4
+  // apart of the same rows, and this keeps what the LDS serves together on
+  // distinct banks (a 16-byte row pad left conflict stalls).
+  auto xsw = [](int r) { return (r & 3) | ((r & 4) << 1); };
   constexpr int XP = (BM * 16 + NT - 1) / NT;  // 16-byte X pieces per thread per chunk
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDSROW];
 
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
     const int piece = min(threadIdx.x + NT * i, BM * 16 - 1);   // BM rows x 16 pieces
     const int row = piece >> 4, part = piece & 15;
     xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + part * 8;
-    xdst[i] = row * LDSROW + part * 8;
+    xdst[i] = row * LDSROW + (part ^ xsw(row)) * 8;
   }
 
   f32x4 acc[NBW][MB];
@@ -314,12 +319,13 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
     for (int i = 0; i < XP; ++i) *reinterpret_cast<uint4*>(&xs[buf][xdst[i]]) = xr[i];
   };
   auto mma = [&](const uint4 (&w)[NBW][4], int buf) {
-    const uint16_t* xb = &xs[buf][r16 * LDSROW + 32 * g4];
+    const uint16_t* xb = &xs[buf][r16 * LDSROW];
+    const int sw = xsw(r16);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * s);
+        const uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * ((4 * g4 + s) ^ sw));
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[nb][mb] = mfma16x16x32(w[nb][s], b, acc[nb][mb]);
       }
@@ -395,8 +401,11 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 // stream in 32-wide K slices through a 4-deep LDS ring filled by direct
 // global->LDS loads: three slices are in flight while one is multiplied, with
 // no staging registers.  A slice row is 64 bytes; its four 16-byte chunks are
-// XOR-swizzled by (row >> 2) & 3, so the fragment reads of 8 consecutive lanes
-// (8 rows, one chunk each) hit distinct banks.  One barrier per slice.
+// XOR-swizzled by (row >> 1) & 3.  A fragment read has lanes 16 apart read two
+// chunks of the same row; with this swizzle the rows and chunks that the LDS
+// serves together land on distinct banks (bank-conflict counters read zero;
+// swizzling by (row >> 2) & 3 left the LDS stalled on conflicts about half
+// of its busy time).  One barrier per slice.
 // Each DMA issue fills a 1 KB region (16 rows x 64 bytes); the regions of a
 // slice go round-robin to the 4 waves (a wave short of a region repeats the
 // last one, writing identical bytes), so every wave issues the same count.
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   for (int j = 0; j < XPW; ++j) {
     const int r = min(wave + NW * j, XR - 1);
     const int row = 16 * r + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    const int ch = (lane & 3) ^ ((row >> 1) & 3);
     xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch;
     xoff[j] = (uint32_t)(r * 1024);
   }
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   for (int j = 0; j < WPW; ++j) {
     const int r = min(wave + NW * j, WR - 1);
     const int row = 16 * r + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    const int ch = (lane & 3) ^ ((row >> 1) & 3);
     wsrc[j] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ch;
     woff[j] = (uint32_t)(r * 1024);
   }
@@ -463,12 +472,12 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb) {
       const int row = wn * 16 * WNB + 16 * nb + r16;
-      a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * (g4 ^ ((row >> 2) & 3))]);
+      a[nb] = *reinterpret_cast<const uint4*>(&wsm[buf][row * BK + 8 * (g4 ^ ((row >> 1) & 3))]);
     }
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) {
       const int row = wm * 16 * WMB + 16 * mb + r16;
-      bx[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * (g4 ^ ((row >> 2) & 3))]);
+      bx[mb] = *reinterpret_cast<const uint4*>(&xs[buf][row * BK + 8 * (g4 ^ ((row >> 1) & 3))]);
     }
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
