@@ -53,6 +53,9 @@ typedef enum {
 
 typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;   /* logits are always f32 */
 typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_mode;
+/* root_mode of medusa_topk / medusa_topk_tree only: root[] is an input (the
+ * previous step's next token, see medusa_next_hidden). */
+#define MEDUSA_ROOT_GIVEN 2
 
 /* Limits of this build. */
 #define MEDUSA_MAX_HEADS 16     /* Medusa heads K */
@@ -110,6 +113,8 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
  *              The sums are taken over 64 vocabulary slices and combined, so
  *              a draw can differ from a serial float64 running sum only when
  *              u * sum lies within rounding of a running sum.
+ *              ROOT_GIVEN: root[] holds the root tokens on entry (the next
+ *              token the previous step produced) and is left as it is.
  *   root   [b] i32; idx [b, K, kmax] i32 (descending; -1 past k_i);
  *   val    [b, K, kmax] f32 (the logits; -inf past k_i)
  *   ws     medusa_topk_workspace bytes: the float64 sampler's per-slice
@@ -278,6 +283,34 @@ size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype
 int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
                          int32_t dtype, int32_t mode, float temperature, float* logits, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_kv_append / medusa_next_hidden - state carried between steps.
+ * [glossary] (decoding loop; speculative KV cache): the tree's key/value
+ * entries join the cache behind the accepted prefix for the verification
+ * pass, and the next step drafts from the hidden state at the last accepted
+ * position; [deep-dive] "What this deep dive assumes": the heads run off one
+ * hidden state.
+ *
+ * medusa_kv_append, per sequence s with P = seq_len[s] (device):
+ *   Kc[s, g, P + j, :] = Knew[s, g, j, :]   j = 0..T-1, every kv head g
+ *   (same for Vc / Vnew).  Knew, Vnew [b, nkv, T, d] in the cache dtype; the
+ *   cache is [b, nkv, Pmax, d].  seq_len is not changed.  A sequence with
+ *   P < 0 or P + T > Pmax is left untouched.  Requires d * sizeof(dtype) % 16
+ *   == 0 and 16-byte aligned buffers.
+ * medusa_next_hidden, per sequence s:
+ *   h[s, :] = O[s, path[s, L[s]], :]          O [b, T, H], h [b, H] (dtype)
+ *   i.e. the verification state of the chosen node (path and L as written by
+ *   medusa_accept / medusa_accept_compact; O as from medusa_tree_attn).  The
+ *   next step's root is that step's bonus token (root_mode MEDUSA_ROOT_GIVEN
+ *   with root = bonus).  Invalid L or path entries leave h[s] untouched.
+ *   Requires H * sizeof(dtype) % 16 == 0 and 16-byte aligned O and h.
+ * ------------------------------------------------------------------------- */
+int medusa_kv_append(void* Kc, void* Vc, const int32_t* seq_len, const void* Knew,
+                     const void* Vnew, int32_t b, int32_t nkv, int32_t Pmax, int32_t T, int32_t d,
+                     int32_t dtype, void* stream);
+int medusa_next_hidden(const void* O, const int32_t* path, const int32_t* L, int32_t b,
+                       int32_t T, int32_t K, int32_t H, int32_t dtype, void* h, void* stream);
 
 #ifdef __cplusplus
 }

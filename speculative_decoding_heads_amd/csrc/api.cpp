@@ -160,8 +160,8 @@ int medusa_topk(const float* logits, int32_t b, int32_t K, int32_t V, const int3
   if (int s = check_k(k_host, K, kmax)) return s;
   for (int i = 0; i < K; ++i)
     if (k_host[i] > V) return fail(MEDUSA_ERR_ARG, "k_i exceeds V");
-  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL)
-    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY or TYPICAL");
+  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL && root_mode != MEDUSA_ROOT_GIVEN)
+    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY, TYPICAL or ROOT_GIVEN");
   if (root_mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
     return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
   if (b == 0) return MEDUSA_OK;
@@ -251,8 +251,8 @@ int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const
   if (int s = check_k(k_host, K, kmax)) return s;
   for (int i = 0; i < K; ++i)
     if (k_host[i] > V) return fail(MEDUSA_ERR_ARG, "k_i exceeds V");
-  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL)
-    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY or TYPICAL");
+  if (root_mode != MEDUSA_GREEDY && root_mode != MEDUSA_TYPICAL && root_mode != MEDUSA_ROOT_GIVEN)
+    return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY, TYPICAL or ROOT_GIVEN");
   if (root_mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
     return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
   std::shared_ptr<const TreePlanHost> p;
@@ -416,6 +416,37 @@ int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
   return hip_status(run_kv_compact(Kc, Vc, seq_len, path, L, b, nkv, Pmax, d, K, dtype,
                                    as_stream(stream)),
                     "kv_compact");
+}
+
+// ------------------------------------------------------------------- state between steps
+int medusa_kv_append(void* Kc, void* Vc, const int32_t* seq_len, const void* Knew,
+                     const void* Vnew, int32_t b, int32_t nkv, int32_t Pmax, int32_t T, int32_t d,
+                     int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (b < 0 || nkv < 1 || d < 1 || T < 1 || T > MEDUSA_MAX_T || Pmax < T)
+    return fail(MEDUSA_ERR_ARG, "need b >= 0, nkv >= 1, d >= 1, 1 <= T <= 256, Pmax >= T");
+  if ((d * elem_size(dtype)) % 16 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d * sizeof(dtype) must be a multiple of 16");
+  if ((int64_t)b * nkv > INT32_MAX) return fail(MEDUSA_ERR_UNSUPPORTED, "b * nkv too large");
+  if (b == 0) return MEDUSA_OK;
+  if (!Kc || !Vc || !seq_len || !Knew || !Vnew) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(Kc) || !aligned16(Vc) || !aligned16(Knew) || !aligned16(Vnew))
+    return fail(MEDUSA_ERR_ARG, "cache and new rows must be 16-byte aligned");
+  return hip_status(run_kv_append(Kc, Vc, seq_len, Knew, Vnew, b, nkv, Pmax, T, d, dtype,
+                                  as_stream(stream)),
+                    "kv_append");
+}
+
+int medusa_next_hidden(const void* O, const int32_t* path, const int32_t* L, int32_t b,
+                       int32_t T, int32_t K, int32_t H, int32_t dtype, void* h, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (b < 0 || T < 1 || T > MEDUSA_MAX_T || H < 1) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256, H >= 1");
+  if (K < 0 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [0, 16]");
+  if ((H * elem_size(dtype)) % 16 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "H * sizeof(dtype) must be a multiple of 16");
+  if (b == 0) return MEDUSA_OK;
+  if (!O || !path || !L || !h) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(O) || !aligned16(h)) return fail(MEDUSA_ERR_ARG, "O and h must be 16-byte aligned");
+  return hip_status(run_next_hidden(O, path, L, b, T, K, H, dtype, h, as_stream(stream)),
+                    "next_hidden");
 }
 
 }  // extern "C"

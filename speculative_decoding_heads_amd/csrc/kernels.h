@@ -8,7 +8,7 @@
 namespace medusa {
 
 enum { kF32 = 0, kBF16 = 1 };
-enum { kGreedy = 0, kTypical = 1 };
+enum { kGreedy = 0, kTypical = 1, kRootGiven = 2 };   // kRootGiven: root_mode only
 
 constexpr int kMaxHeads = 16;   // Medusa heads K
 constexpr int kMaxK = 16;       // shortlist size per head
@@ -107,6 +107,13 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
                       const KvRollback* kv = nullptr, const void* parts = nullptr);
 
 // ---- compaction (compact.hip)
+// ---- state between steps (loop.hip)
+hipError_t run_kv_append(void* Kc, void* Vc, const int* seq_len, const void* Knew,
+                         const void* Vnew, int b, int nkv, int Pmax, int T, int d, int dtype,
+                         hipStream_t st);
+hipError_t run_next_hidden(const void* O, const int* path, const int* L, int b, int T, int K,
+                           int H, int dtype, void* h, hipStream_t st);
+
 hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,
                           int nkv, int Pmax, int d, int K, int dtype, hipStream_t st);
 

@@ -6,7 +6,8 @@
 //
 // Selection is one launch, one workgroup per row (see topk_rows).
 // The root row (head 0) takes k = 1 in greedy mode; in typical mode the root
-// is drawn by the row sampler instead.
+// is drawn by the row sampler instead, and with a given root (the previous
+// step's next token) root[] is an input.
 //
 // The row sampler (run_sample_rows) draws from softmax(x / T) in float64:
 // e_i = exp((x_i - max)/T), the smallest i whose running sum (vocabulary
@@ -99,8 +100,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
     }
   }
   const bool tree = to.tokens != nullptr;
-  if (k == 0) {            // typical root row: drawn by sample_rows
-    if (tree && i == 0) tree_common(t, to, s);
+  if (k == 0) {            // root row: drawn by the sampler (typical) or given
+    if (tree && i == 0) {
+      tree_common(t, to, s);
+      if (a.root_mode == kRootGiven && tid == 0) to.tokens[(int64_t)s * t.T] = root[s];
+    }
     return;
   }
   if (tid == 0) ncand = 0;

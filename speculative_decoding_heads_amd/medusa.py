@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmedusa.so")
 
 F32, BF16 = 0, 1
 GREEDY, TYPICAL = 0, 1
+ROOT_GIVEN = 2          # root_mode only: root[] is an input
 MAX_T = 256
 
 _lib = None
@@ -62,6 +63,8 @@ _SIGS = {
                               _I32),
     "medusa_verify_workspace": ([_I64, _I32, _I32, _I32, _I32], _SZ),
     "medusa_verify_logits": ([_P, _I64, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ, _P], _I32),
+    "medusa_kv_append": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
+    "medusa_next_hidden": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -358,3 +361,34 @@ def medusa_verify_logits(x, LM, logits, mode, temperature, ws, stream=None):
                                     _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
                                     _stream(stream))
     _check("medusa_verify_logits", st)
+
+
+def medusa_kv_append(Kc, Vc, seq_len, Knew, Vnew, stream=None):
+    """Tree K/V [b, nkv, T, d] into cache slots seq_len .. seq_len+T-1."""
+    b, nkv, Pmax, d = Kc.shape
+    _cache_shapes(Kc, Vc, seq_len, b)
+    _need(Knew.dim() == 4 and Knew.shape[0] == b and Knew.shape[1] == nkv and Knew.shape[3] == d,
+          "Knew: expected [b, nkv, T, d]")
+    _shape(Vnew, tuple(Knew.shape), "Vnew")
+    _dt(Knew, Kc.dtype, "Knew")
+    _dt(Vnew, Kc.dtype, "Vnew")
+    T = Knew.shape[2]
+    st = lib().medusa_kv_append(_ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(Knew), _ptr(Vnew), b, nkv,
+                                Pmax, T, d, dtype_code(Kc), _stream(stream))
+    _check("medusa_kv_append", st)
+
+
+def medusa_next_hidden(O, path, L, h, stream=None):
+    """h[s] = O[s, path[s, L[s]]] (O [b, T, H] or [b, T, nq, d]; h [b, H])."""
+    b, T = O.shape[0], O.shape[1]
+    H = O[0, 0].numel()
+    K = path.shape[1] - 1
+    _shape(path, (b, K + 1), "path")
+    _shape(L, (b,), "L")
+    _dt(path, torch.int32, "path")
+    _dt(L, torch.int32, "L")
+    _need(h.numel() == b * H and h.shape[0] == b, "h: expected [b, H]")
+    _dt(h, O.dtype, "h")
+    st = lib().medusa_next_hidden(_ptr(O), _ptr(path), _ptr(L), b, T, K, H, dtype_code(O), _ptr(h),
+                                  _stream(stream))
+    _check("medusa_next_hidden", st)

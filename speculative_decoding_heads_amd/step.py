@@ -59,16 +59,21 @@ class VerifyStep:
         self.ws_verify = M.workspace(
             M.medusa_verify_workspace(c.b * T, c.nq * c.d, c.V, dt, self.mode), device)
 
-    def run(self, x, step=0, stream=None, fused=True):
-        """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len."""
+    def run(self, x, step=0, stream=None, fused=True, root_given=False):
+        """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len.
+
+        root_given: the tree root is the previous step's next token (self.bonus)
+        instead of the base head's argmax / sample (fused path only)."""
         c = self.cfg
         M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
                        stream=stream)
         if fused:
             M.medusa_topk_tree(self.logits, c.k, c.kmax, self.N, c.decay.numerator,
-                               c.decay.denominator, self.mode, c.temperature, c.seed, step,
-                               x["seq_len"], self.root, self.idx, self.val, self.tokens, self.pos,
-                               self.parent, self.depth, self.anc, self.ws_topk, stream=stream)
+                               c.decay.denominator, M.ROOT_GIVEN if root_given else self.mode,
+                               c.temperature, c.seed, step, x["seq_len"],
+                               self.bonus if root_given else self.root, self.idx, self.val,
+                               self.tokens, self.pos, self.parent, self.depth, self.anc,
+                               self.ws_topk, stream=stream)
         else:
             M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step,
                           self.root, self.idx, self.val, self.ws_topk, stream=stream)
@@ -93,6 +98,56 @@ class VerifyStep:
                             c.temperature, c.eps, c.delta, c.seed, step, self.L, self.path,
                             self.acc_tokens, self.bonus, self.ws_acc, stream=stream)
             M.medusa_kv_compact(x["Kc"], x["Vc"], x["seq_len"], self.path, self.L, stream=stream)
+
+
+class VerifyLoop:
+    """Consecutive steps with the state carried on the device (the decoding
+    loop of inferensys.com "Medusa Heads"): before step s the step's tree K/V
+    join the cache behind the accepted prefix (medusa_kv_append); the step runs
+    the five fused calls, step s >= 1 with the previous step's next token as
+    the tree root; after it the chosen node's verification state becomes the
+    next hidden state (medusa_next_hidden).  seq_len advances by L + 1 per step
+    (the compaction).  The tree Q / K / V of each step are inputs (the
+    backbone that would produce them is not part of this path).
+
+    Every call only enqueues kernels, so ``run`` can be captured in a HIP
+    graph (``capture``) and replayed."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.step = VerifyStep(cfg, device)
+
+    def run(self, x, Qs, Kn, Vn, step0=0, root_given_first=False, stream=None, after_step=None):
+        """x: h, W, LM, Kc, Vc, seq_len (state, updated in place); Qs [S, b, T, nq, d],
+        Kn / Vn [S, b, nkv, T, d].  after_step(s) runs after each step (eager use only)."""
+        st = self.step
+        for s in range(Qs.shape[0]):
+            M.medusa_kv_append(x["Kc"], x["Vc"], x["seq_len"], Kn[s], Vn[s], stream=stream)
+            xs = dict(x)
+            xs["Q"] = Qs[s]
+            st.run(xs, step=step0 + s, stream=stream, root_given=(s > 0 or root_given_first))
+            M.medusa_next_hidden(st.O, st.path, st.L, x["h"], stream=stream)
+            if after_step is not None:
+                after_step(s)
+
+    def capture(self, x, Qs, Kn, Vn, step0=0, root_given_first=False):
+        """A torch CUDA (HIP) graph of ``run``; replaying it advances the state."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run(x, Qs, Kn, Vn, step0=step0, root_given_first=root_given_first)
+        return g
+
+
+def loop_inputs(cfg, steps, seed_base=0, device="cuda"):
+    """Seeded per-step tree Q / K / V for ``VerifyLoop`` (N(0, 1), rounded to the
+    workload dtype): Qs [S, b, T, nq, d], Kn / Vn [S, b, nkv, T, d]."""
+    from .synth import normal
+    c = cfg
+    Qs = normal((steps, c.b, c.T, c.nq, c.d), seed_base + 101, 1.0, c.dtype)
+    Kn = normal((steps, c.b, c.nkv, c.T, c.d), seed_base + 102, 1.0, c.dtype)
+    Vn = normal((steps, c.b, c.nkv, c.T, c.d), seed_base + 103, 1.0, c.dtype)
+    return Qs.to(device), Kn.to(device), Vn.to(device)
 
 
 def device_inputs(cfg, host, device="cuda"):

@@ -29,12 +29,15 @@ def seed_of(workload, tensor_id, chunk=0):
 
 
 def normal(shape, seed, std=1.0, dtype="f32"):
-    """N(0, std^2) float32 draws, optionally rounded to bf16, as a CPU tensor."""
+    """N(0, std^2) float32 draws, optionally rounded to bf16, as a CPU tensor.
+    dtype: "f32" / "bf16" or torch.float32 / torch.bfloat16."""
+    if dtype not in ("f32", "bf16", torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported dtype {dtype!r}")
     g = torch.Generator().manual_seed(seed)
     x = torch.randn(*shape, generator=g, dtype=torch.float32)
     if std != 1.0:
         x.mul_(std)
-    return x.to(torch.bfloat16) if dtype == "bf16" else x
+    return x.to(torch.bfloat16) if dtype in ("bf16", torch.bfloat16) else x
 
 
 def _chunked(shape, workload, name, std, dtype):
