@@ -18,6 +18,11 @@ region.  When a workload's weights+cache are small enough to sit in the
 A second pass of K steps records events between the calls for the per-call
 breakdown and the roofline of the dominant kernel.
 
+With --loop S (default 8) the workload also runs as a steady-state loop: S
+consecutive steps with the state carried on the device, captured in one HIP
+graph and replayed (reported under "loop"; `value` stays the single-step
+figure above).
+
 Prints ONE JSON line (rank 0).  --gpus N > 1 exits with a message: this build
 runs on one GPU.
 """
@@ -142,6 +147,42 @@ def measure(cfg, steps, warmup, rotate=None, log=print):
     return ms, per_call
 
 
+def measure_loop(cfg, steps_per_graph, replays, warmup_replays=2, log=print):
+    """Steady-state loop (VerifyLoop): steps_per_graph consecutive steps with the
+    state carried on the device (tree K/V appended behind the accepted prefix,
+    next hidden state and root from the previous step), captured once in a HIP
+    graph and replayed; the state keeps advancing across replays, so the cache
+    holds every replay's steps.  Returns ms per step."""
+    import torch
+    from speculative_decoding_heads_amd.step import VerifyLoop, device_inputs, loop_inputs
+    from speculative_decoding_heads_amd.synth import make_inputs
+
+    c = cfg
+    x = device_inputs(c, make_inputs(c))
+    total = (warmup_replays + replays) * steps_per_graph
+    cap = c.P + total * (c.K + 1) + c.T
+    for name in ("Kc", "Vc"):
+        big = torch.zeros(c.b, c.nkv, cap, c.d, dtype=x[name].dtype, device="cuda")
+        big[:, :, : c.P] = x[name][:, :, : c.P]
+        x[name] = big
+    Qs, Kn, Vn = loop_inputs(c, steps_per_graph, seed_base=c.index)
+    loop = VerifyLoop(c)
+    g = loop.capture(x, Qs, Kn, Vn)
+    for _ in range(warmup_replays):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (replays * steps_per_graph)
+    log(f"[bench] {c.name}: loop of {steps_per_graph} steps x {replays} graph replays, "
+        f"{ms * 1e3:.1f} us per step, final seq_len {x['seq_len'].tolist()[:4]}")
+    return ms
+
+
 def cpu_baseline(cfg, seconds, log=print):
     """The oracle (numpy float64) timed on this host on whole steps of the workload."""
     import numpy as np
@@ -249,6 +290,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop", type=int, default=8,
+                    help="steps per captured graph for the steady-state loop (0 to skip)")
+    ap.add_argument("--loop-replays", type=int, default=10)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured copy / read / vendor-GEMM reference rates")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -308,6 +352,12 @@ def main():
                        "unit": "verify-steps/s", "ms_per_step": round(ms2, 4),
                        "step_effective_GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
                        "per_call_us": {k: round(v, 2) for k, v in pc2.items()}}
+    if args.loop > 0:
+        ms_l = measure_loop(cfg, args.loop, args.loop_replays, log=log)
+        out["loop"] = {"workload": cfg.name, "value": round(1000.0 / ms_l, 2),
+                       "unit": "verify-steps/s", "ms_per_step": round(ms_l, 4),
+                       "steps_per_graph": args.loop, "replays": args.loop_replays,
+                       "hip_graph": True}
     torch.cuda.synchronize()
     out["measured_peaks"] = None if args.no_peaks else measured_peaks(log)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds, log)
