@@ -122,6 +122,22 @@ def test_validation_before_launch():
     # compaction: row size not a multiple of 16 bytes
     assert L.medusa_kv_compact(fake, fake, fake, fake, fake, 1, 1, 10, 6, 2, 1, None) == ERR_UNSUPPORTED
     assert b"16" in L.medusa_last_error()
+    # root modes: GREEDY, TYPICAL, ROOT_GIVEN (2) only
+    assert L.medusa_topk(fake, 1, 2, 100, k, 4, 3, 1.0, 0, 0, fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert b"ROOT_GIVEN" in L.medusa_last_error()
+    # tree K/V append: T > Pmax, T out of range, row size, alignment; b == 0 is a no-op
+    assert L.medusa_kv_append(fake, fake, fake, fake, fake, 1, 2, 10, 11, 64, 1, None) == ERR_ARG
+    assert L.medusa_kv_append(fake, fake, fake, fake, fake, 1, 2, 400, 300, 64, 1, None) == ERR_ARG
+    assert L.medusa_kv_append(fake, fake, fake, fake, fake, 1, 2, 100, 11, 6, 1, None) == ERR_UNSUPPORTED
+    assert L.medusa_kv_append(fake, fake, fake, ctypes.c_void_p(0x1008), fake, 1, 2, 100, 11, 64, 1,
+                              None) == ERR_ARG
+    assert L.medusa_kv_append(None, None, None, None, None, 0, 2, 100, 11, 64, 1, None) == 0
+    # next hidden state: K, H row size, alignment, NULL; b == 0 is a no-op
+    assert L.medusa_next_hidden(fake, fake, fake, 1, 11, 17, 256, 1, fake, None) == ERR_ARG
+    assert L.medusa_next_hidden(fake, fake, fake, 1, 11, 3, 100, 1, fake, None) == ERR_UNSUPPORTED
+    assert L.medusa_next_hidden(fake, fake, fake, 1, 11, 3, 256, 1, ctypes.c_void_p(0x1004), None) == ERR_ARG
+    assert L.medusa_next_hidden(fake, None, fake, 1, 11, 3, 256, 1, fake, None) == ERR_ARG
+    assert L.medusa_next_hidden(None, None, None, 0, 11, 3, 256, 1, None, None) == 0
 
 
 def test_workspace_queries_are_host_only_and_sized():
