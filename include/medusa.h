@@ -88,7 +88,10 @@ const char* medusa_last_error(void);
  *   logits  [rows, R, V] f32     logits[r, j, :] = LM . u[r, j, :]
  * bf16 needs H % 128 == 0 and 16-byte aligned x, W, LM, u_out.  rows == 0 is
  * a no-op.  Arithmetic: bf16 operands, f32 accumulation (MFMA); f32 path in
- * f32 throughout.
+ * f32 throughout.  With n_heads > 0 the bf16 LM projection sums the K chunks
+ * in the reverse order of the n_heads = 0 call (so a step's two passes over
+ * LM each begin on the weights the other read last, still in the last-level
+ * cache); logits of the same row from the two forms can differ by rounding.
  * ------------------------------------------------------------------------- */
 size_t medusa_heads_workspace(int64_t rows, int32_t H, int32_t n_heads, int32_t include_base,
                               int32_t dtype);

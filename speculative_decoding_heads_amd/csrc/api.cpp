@@ -105,7 +105,11 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
     if (s) return s;
     gemm_x = u;
   }
-  return hip_status(run_lm_logits(gemm_x, (int)(rows * R), H, LM, V, dtype, logits, st),
+  // Head rows walk the LM weights' K chunks backwards, verify rows (n_heads =
+  // 0) forwards: a step's two LM passes then each start on what the other
+  // read last, which the last-level cache still holds.
+  return hip_status(run_lm_logits(gemm_x, (int)(rows * R), H, LM, V, dtype, logits, st,
+                                  n_heads > 0),
                     "LM projection");
 }
 

@@ -255,7 +255,8 @@ template <int MB, int NBW, class Epi, int NWAVES = 4>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* __restrict__ X,
                                                                int64_t ldx, int M,
                                                                const uint16_t* __restrict__ W,
-                                                               int N, int Kd, int ntm, Epi epi) {
+                                                               int N, int Kd, int ntm, Epi epi,
+                                                               bool rev) {
   constexpr int NT = 64 * NWAVES;
   constexpr int BM = 16 * MB;
   constexpr int BN = 16 * NBW * NWAVES;
@@ -300,8 +301,14 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
   // Each workgroup walks the K chunks from its own starting chunk: every
   // workgroup reads the same activation rows, and in lockstep they would all
   // hit the same few L2 channels at once.
+  // With rev the walk runs backwards (rot-1, rot-2, ..., rot): the same grid
+  // over the same weights then reads, first, what the forward walk read last.
   const int rot = (int)(blockIdx.x % (unsigned)nchunks);
-  auto rc = [&](int c) { const int q = c + rot; return q >= nchunks ? q - nchunks : q; };
+  auto rc = [&](int c) {
+    if (rev) { const int q = rot - 1 - c; return q < 0 ? q + nchunks : q; }
+    const int q = c + rot;
+    return q >= nchunks ? q - nchunks : q;
+  };
   uint4 wa[NBW][4], wb[NBW][4], xr[XP];
   auto loadW = [&](int c, uint4 (&w)[NBW][4]) {
     const int k0 = rc(c) << 7;
@@ -631,7 +638,7 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
 
 template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
-                              int Kd, const Epi& epi, hipStream_t st) {
+                              int Kd, const Epi& epi, hipStream_t st, bool rev = false) {
   // logits always take the tiled / ring kernels, so the verify-rows logits of
   // medusa_heads and medusa_verify_logits come from the same kernel
   const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
@@ -667,7 +674,7 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
   do {                                                                                         \
     const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
     hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * p.ntiles), dim3(64 * NW_), \
-                       0, st, X, ldx, M, W, N, Kd, ntm, epi);                                  \
+                       0, st, X, ldx, M, W, N, Kd, ntm, epi, rev);                             \
   } while (0)
 #define TILED(MB_)                                                                             \
   do {                                                                                         \
@@ -729,11 +736,11 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
 }
 
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st) {
+                         float* logits, hipStream_t st, bool rev) {
   EpiLogits epi{logits, (int64_t)V, M, V};
   if (dtype == kBF16)
     return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
-                       H, epi, st);
+                       H, epi, st, rev);
   return launch_f32(static_cast<const float*>(x), H, M, static_cast<const float*>(LM), V, H, epi,
                     st);
 }

@@ -18,8 +18,10 @@ constexpr int kMaxAncWords = kMaxT / 64;
 // ---- heads / LM projection (gemm.hip)
 hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_heads, int dtype,
                             void* u, int R, int base, hipStream_t st);
+// rev: the weight-streaming kernel walks K backwards (same products, another
+// summation order); see medusa_heads.
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st);
+                         float* logits, hipStream_t st, bool rev = false);
 // LM projection of the verify rows plus acceptance partials per (row, weight
 // tile) in ws: header (kPartsHeader bytes: ntiles, typical, rows), then
 // [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).
