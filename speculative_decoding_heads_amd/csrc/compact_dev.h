@@ -46,7 +46,8 @@ __device__ __forceinline__ void compact_columns(uint8_t* __restrict__ Kc, uint8_
       const int g = rem / cols, c = rem - g * cols;
       base[j] = (which ? Vc : Kc) + ((int64_t)s * nkv + g) * slab + (int64_t)c * 16;
     }
-    for (int d0 = 0; d0 <= L; d0 += 4) {
+    // the root never moves (path[0] = 0): start the groups of four at depth 1
+    for (int d0 = pth[0] == 0 ? 1 : 0; d0 <= L; d0 += 4) {
       int src[4];
       bool mv[4];
 #pragma unroll
