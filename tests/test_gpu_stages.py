@@ -82,6 +82,27 @@ def test_zero_head_weights_reduce_to_base_head_bitwise(dt):
     assert_rows_close(np64(logits[:, 0]), ref, TOL_BF16 if dt == "bf16" else TOL_F32, "base")
 
 
+@pytest.mark.parametrize("b,H,V", [(1, 2048, 3000), (1, 1024, 32000), (3, 1536, 32003)])
+def test_head_rows_and_base_rows_differ_only_in_summation_order(b, H, V):
+    """With n_heads > 0 the LM projection walks K backwards (the n_heads = 0
+    call forwards): slot 0 of the head call and the base-only call project the
+    same x through the same bf16 products, summed in another order."""
+    K = 4
+    h = normal((b, H), 31 * b + H, 1.0, torch.bfloat16)
+    W = normal((K, H, H), 32 * b + H, 0.02, torch.bfloat16)
+    LM = normal((V, H), 33 * b + H, 0.02, torch.bfloat16)
+    logits = torch.empty(b, K + 1, V, dtype=torch.float32, device=DEV)
+    base = torch.empty(b, V, dtype=torch.float32, device=DEV)
+    u = torch.empty(b, K + 1, H, dtype=torch.bfloat16, device=DEV)
+    hd, LMd = h.to(DEV), LM.to(DEV)
+    M.medusa_heads(hd, W.to(DEV), LMd, logits, include_base=1, u_out=u)
+    M.medusa_heads(hd, None, LMd, base, include_base=1)
+    torch.cuda.synchronize()
+    a, c = np64(logits[:, 0]), np64(base)
+    assert_rows_close(a, c, 2e-6, "slot 0 vs base-only")
+    assert_rows_close(c, lm_project(np64(h), np64(LM)), 2e-5, "base-only")
+
+
 @pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 2000), (11, 256, 4096),
                                        (2080, 384, 1000), (300, 128, 777), (97, 512, 300),
                                        (5, 384, 31000), (65, 256, 30977), (16, 640, 33000),
