@@ -246,6 +246,9 @@ ATTN_CASES = [
     (3, (2, 2), None, 2, 2, 64, 0, "bf16"),           # no prefix: tree only
     (2, (16, 15), 255, 2, 1, 128, 64, "bf16"),        # 256 nodes: 4 anc words
     (1, (1,), 0, 2, 2, 128, 5000, "bf16"),            # root only, long prefix
+    (1, (10,) * 4, 64, 6, 2, 128, 700, "bf16"),       # GQA 3, 195 rows: 4 waves x 4 blocks
+    (1, (10,) * 4, 64, 4, 2, 64, 300, "bf16"),        # d 64, 130 rows: 4 waves x 3 blocks
+    (2, (10,) * 4, 64, 16, 2, 64, 500, "bf16"),       # d 64, 520 rows: 4 waves x 6 blocks, 2 groups
 ]
 
 
