@@ -18,6 +18,9 @@ Sources (web pages on Medusa heads; cited by page title and section):
     longest prefix matching what the model would have produced.
   * zackli.ai, "Speculative Decoding Deep Dive II: Medusa, MTP" (section
     "Medusa"): Anc(i), full-path and tree-node counts; head indexing.
+  * aicassindra.com "Medusa deep dive", "What it costs on a CPU-bound SLM":
+    expected acceptance length as the throughput multiplier, the tree size as
+    a tuned budget (module ``budget``).
 
 Every function states the passage it follows and, where the pages leave a step
 open, the reading taken.  Pins: ``tests/test_oracle_*.py``.
@@ -32,6 +35,7 @@ from .attention import tree_attention, path_attention
 from .accept import accept_greedy_walk, accept_greedy_parallel, accept_typical, typical_local
 from .compact import kv_compact
 from .step import oracle_step
+from .budget import tree_plan_rates, expected_tokens, plan_from_tables, accept_tally
 
 __all__ = [
     "round_bf16", "heads", "lm_project", "topk_stable", "argmax_lowest",
@@ -39,4 +43,5 @@ __all__ = [
     "full_tree_node_count", "full_path_count", "TreePlan", "tree_attention",
     "path_attention", "accept_greedy_walk", "accept_greedy_parallel",
     "accept_typical", "typical_local", "kv_compact", "oracle_step",
+    "tree_plan_rates", "expected_tokens", "plan_from_tables", "accept_tally",
 ]
