@@ -315,6 +315,61 @@ int medusa_kv_append(void* Kc, void* Vc, const int32_t* seq_len, const void* Kne
 int medusa_next_hidden(const void* O, const int32_t* path, const int32_t* L, int32_t b,
                        int32_t T, int32_t K, int32_t H, int32_t dtype, void* h, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The tree budget: medusa_tree_plan_rates (host only), medusa_topk_tree_tables,
+ * medusa_accept_tally.
+ * [deep-dive] "From top-k heads to a sparse candidate tree": the tree shape is
+ * a tuned budget, more candidates (higher acceptance) against a heavier pass;
+ * "What it costs on a CPU-bound SLM": the expected acceptance length (tokens
+ * confirmed per pass) multiplies throughput; "The conditional-independence
+ * gap": every head sees the same hidden state and nothing else.
+ *
+ * Rates q [K][MEDUSA_MAX_K] f64 (row d = head d+1, column r = rank r; entries
+ * r >= k_d ignored, the rest in [0, 1]): q[d][r] is the rate at which the
+ * rank-r candidate of head d+1 is accepted when its parent was.  With heads
+ * independent given the hidden state, candidate (r_1..r_D) is accepted with
+ * probability q[0][r_1] * ... * q[D-1][r_D] (f64, in that order).
+ *
+ * medusa_tree_plan_rates keeps the N candidates of largest probability under
+ * (probability descending, D ascending, tuple ascending) -- the N-candidate
+ * tree of most expected tokens, closed under ancestors since q <= 1 -- and
+ * returns the tree as medusa_tree_plan does (host arrays, same node order)
+ * plus *expected_tokens = 1 + the kept probabilities summed in node order.
+ * N = -1 keeps all.  The fixed rule of medusa_tree_plan is the case
+ * q[d][r] = decay^(d+1) / (r + 1) (up to the order of exact ties).
+ *
+ * medusa_topk_tree_tables is medusa_topk_tree for a tree given by host
+ * tables plan_parent / plan_rank [T] (as filled by either planner): node 0
+ * the root (parent -1), 0 <= parent[i] < i, depths (derived from the parents)
+ * never decreasing along the node order and <= K, rank[i] < k of its head,
+ * no two children of one node with the same rank.  Outputs as
+ * medusa_topk_tree for that tree.  MEDUSA_ERR_ARG on an invalid table.
+ *
+ * medusa_accept_tally adds one batch of steps to the counts accepted and
+ * offered [K][MEDUSA_MAX_K] i64 (device, 8-byte aligned, zeroed by the caller
+ * before the first batch; calls add): for sequence s with 0 <= L[s] <= K and
+ * the accepted path path[s, 0..L[s]] (as written by medusa_accept), a node of
+ * depth D and rank r was offered when its parent is path[s, D-1], and accepted
+ * when it is path[s, D]; offered[D-1][r] and accepted[D-1][r] count them.
+ * accepted / offered estimates q.  The tree is given by host tables as for
+ * medusa_topk_tree_tables.  Calls that overlap on one counts buffer add
+ * atomically.
+ * ------------------------------------------------------------------------- */
+int medusa_tree_plan_rates(const int32_t* k_host, int32_t K, int32_t N, const double* q,
+                           int32_t* parent, int32_t* depth, int32_t* rank, int32_t T_cap,
+                           int32_t* T_out, double* expected_tokens);
+int medusa_topk_tree_tables(const float* logits, int32_t b, int32_t K, int32_t V,
+                            const int32_t* k_host, int32_t kmax, const int32_t* plan_parent,
+                            const int32_t* plan_rank, int32_t T, int32_t root_mode,
+                            float temperature, uint64_t seed, uint64_t step,
+                            const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                            int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth,
+                            uint64_t* anc, int32_t anc_words, void* ws, size_t ws_bytes,
+                            void* stream);
+int medusa_accept_tally(const int32_t* L, const int32_t* path, int32_t b, const int32_t* k_host,
+                        int32_t K, const int32_t* plan_parent, const int32_t* plan_rank,
+                        int32_t T, int64_t* accepted, int64_t* offered, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

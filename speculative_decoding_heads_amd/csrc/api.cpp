@@ -243,12 +243,16 @@ int medusa_build_tree(const int32_t* k_host, int32_t K, int32_t N, int32_t decay
 }
 
 // ------------------------------------------------------------------- top-k + tree, one launch
-int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
-                     int32_t kmax, int32_t N, int32_t decay_num, int32_t decay_den,
-                     int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
-                     const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
-                     int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
-                     int32_t anc_words, void* ws, size_t ws_bytes, void* stream) {
+static int topk_tree_common(const float* logits, int32_t b, int32_t K, int32_t V,
+                            const int32_t* k_host, int32_t kmax, int32_t root_mode,
+                            float temperature, uint64_t seed, uint64_t step,
+                            const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                            int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth,
+                            uint64_t* anc, int32_t anc_words, void* ws, size_t ws_bytes,
+                            void* stream, const std::shared_ptr<const TreePlanHost>& p);
+
+static int topk_tree_args(int32_t b, int32_t K, int32_t V, const int32_t* k_host, int32_t kmax,
+                          int32_t root_mode, float temperature) {
   if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
   if (V <= 0) return fail(MEDUSA_ERR_ARG, "V must be positive");
   if (kmax < 1 || kmax > MEDUSA_MAX_K) return fail(MEDUSA_ERR_ARG, "kmax out of range [1, 16]");
@@ -259,8 +263,48 @@ int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const
     return fail(MEDUSA_ERR_ARG, "root_mode must be GREEDY, TYPICAL or ROOT_GIVEN");
   if (root_mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
     return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  return MEDUSA_OK;
+}
+
+int medusa_topk_tree(const float* logits, int32_t b, int32_t K, int32_t V, const int32_t* k_host,
+                     int32_t kmax, int32_t N, int32_t decay_num, int32_t decay_den,
+                     int32_t root_mode, float temperature, uint64_t seed, uint64_t step,
+                     const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                     int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
+                     int32_t anc_words, void* ws, size_t ws_bytes, void* stream) {
+  if (int s = topk_tree_args(b, K, V, k_host, kmax, root_mode, temperature)) return s;
   std::shared_ptr<const TreePlanHost> p;
   if (int s = plan_for(k_host, K, N, decay_num, decay_den, &p)) return s;
+  return topk_tree_common(logits, b, K, V, k_host, kmax, root_mode, temperature, seed, step,
+                          seq_len, root, idx, val, tokens, pos, parent, depth, anc, anc_words, ws,
+                          ws_bytes, stream, p);
+}
+
+int medusa_topk_tree_tables(const float* logits, int32_t b, int32_t K, int32_t V,
+                            const int32_t* k_host, int32_t kmax, const int32_t* plan_parent,
+                            const int32_t* plan_rank, int32_t T, int32_t root_mode,
+                            float temperature, uint64_t seed, uint64_t step,
+                            const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                            int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth,
+                            uint64_t* anc, int32_t anc_words, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (int s = topk_tree_args(b, K, V, k_host, kmax, root_mode, temperature)) return s;
+  if (!plan_parent || !plan_rank) return fail(MEDUSA_ERR_ARG, "plan tables are NULL");
+  std::string err;
+  auto p = plan_from_tables(k_host, K, plan_parent, plan_rank, T, &err);
+  if (!p) return fail(MEDUSA_ERR_ARG, err);
+  return topk_tree_common(logits, b, K, V, k_host, kmax, root_mode, temperature, seed, step,
+                          seq_len, root, idx, val, tokens, pos, parent, depth, anc, anc_words, ws,
+                          ws_bytes, stream, p);
+}
+
+static int topk_tree_common(const float* logits, int32_t b, int32_t K, int32_t V,
+                            const int32_t* k_host, int32_t kmax, int32_t root_mode,
+                            float temperature, uint64_t seed, uint64_t step,
+                            const int32_t* seq_len, int32_t* root, int32_t* idx, float* val,
+                            int32_t* tokens, int32_t* pos, int32_t* parent, int32_t* depth,
+                            uint64_t* anc, int32_t anc_words, void* ws, size_t ws_bytes,
+                            void* stream, const std::shared_ptr<const TreePlanHost>& p) {
   if (anc_words < (p->T + 63) / 64) return fail(MEDUSA_ERR_ARG, "anc_words < ceil(T / 64)");
   if (b == 0) return MEDUSA_OK;
   if (!logits || !root || !idx || !val || !seq_len || !tokens || !pos || !parent || !depth || !anc)
@@ -451,6 +495,62 @@ int medusa_next_hidden(const void* O, const int32_t* path, const int32_t* L, int
   if (!aligned16(O) || !aligned16(h)) return fail(MEDUSA_ERR_ARG, "O and h must be 16-byte aligned");
   return hip_status(run_next_hidden(O, path, L, b, T, K, H, dtype, h, as_stream(stream)),
                     "next_hidden");
+}
+
+// ------------------------------------------------------------------- tree budget
+int medusa_tree_plan_rates(const int32_t* k_host, int32_t K, int32_t N, const double* q,
+                           int32_t* parent, int32_t* depth, int32_t* rank, int32_t T_cap,
+                           int32_t* T_out, double* expected_tokens) {
+  if (int s = check_k(k_host, K, 0)) return s;
+  if (!q) return fail(MEDUSA_ERR_ARG, "q is NULL");
+  if (N < -1) return fail(MEDUSA_ERR_ARG, "N must be >= 0, or -1 for the full tree");
+  for (int d = 0; d < K; ++d)
+    for (int r = 0; r < k_host[d]; ++r) {
+      const double v = q[d * MEDUSA_MAX_K + r];
+      if (!(v >= 0.0 && v <= 1.0)) return fail(MEDUSA_ERR_ARG, "rates must lie in [0, 1]");
+    }
+  const int64_t total = full_tree_candidates(k_host, K);
+  if (N > total && total >= 0) return fail(MEDUSA_ERR_ARG, "N exceeds the candidate count");
+  const int64_t keep = N < 0 ? total : N;
+  if (keep < 0 || keep + 1 > MEDUSA_MAX_T) return fail(MEDUSA_ERR_UNSUPPORTED, "tree exceeds 256 nodes");
+  std::string err;
+  double e = 0.0;
+  auto p = plan_from_rates(k_host, K, N, q, &e, &err);
+  if (!p) return fail(MEDUSA_ERR_UNSUPPORTED, err);
+  if (T_out) *T_out = p->T;
+  if (expected_tokens) *expected_tokens = e;
+  if (!parent && !depth && !rank) return MEDUSA_OK;
+  if (T_cap < p->T) return fail(MEDUSA_ERR_ARG, "T_cap smaller than the tree");
+  for (int i = 0; i < p->T; ++i) {
+    if (parent) parent[i] = p->parent[i];
+    if (depth) depth[i] = p->depth[i];
+    if (rank) rank[i] = p->rank[i];
+  }
+  return MEDUSA_OK;
+}
+
+int medusa_accept_tally(const int32_t* L, const int32_t* path, int32_t b, const int32_t* k_host,
+                        int32_t K, const int32_t* plan_parent, const int32_t* plan_rank,
+                        int32_t T, int64_t* accepted, int64_t* offered, void* stream) {
+  if (int s = check_k(k_host, K, 0)) return s;
+  if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
+  if (!plan_parent || !plan_rank) return fail(MEDUSA_ERR_ARG, "plan tables are NULL");
+  std::string err;
+  auto p = plan_from_tables(k_host, K, plan_parent, plan_rank, T, &err);
+  if (!p) return fail(MEDUSA_ERR_ARG, err);
+  if (b == 0) return MEDUSA_OK;
+  if (!L || !path || !accepted || !offered) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (((uintptr_t)accepted & 7u) || ((uintptr_t)offered & 7u))
+    return fail(MEDUSA_ERR_ARG, "counts must be 8-byte aligned");
+  TreeDev t{};
+  t.T = p->T; t.K = K; t.kmax = MEDUSA_MAX_K; t.anc_words = (p->T + 63) / 64;
+  for (int i = 0; i < p->T; ++i) {
+    t.parent[i] = (int16_t)p->parent[i];
+    t.depth[i] = (uint8_t)p->depth[i];
+    t.rank[i] = (uint8_t)(p->rank[i] < 0 ? 0 : p->rank[i]);
+  }
+  return hip_status(run_accept_tally(L, path, b, K, t, accepted, offered, as_stream(stream)),
+                    "accept_tally");
 }
 
 }  // extern "C"

@@ -115,6 +115,9 @@ hipError_t run_kv_append(void* Kc, void* Vc, const int* seq_len, const void* Kne
                          hipStream_t st);
 hipError_t run_next_hidden(const void* O, const int* path, const int* L, int b, int T, int K,
                            int H, int dtype, void* h, hipStream_t st);
+// offered / accepted counts per (depth - 1, rank), [K][16] int64, added to
+hipError_t run_accept_tally(const int* L, const int* path, int b, int K, const TreeDev& t,
+                            int64_t* accepted, int64_t* offered, hipStream_t st);
 
 hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,
                           int nkv, int Pmax, int d, int K, int dtype, hipStream_t st);

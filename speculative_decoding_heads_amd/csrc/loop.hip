@@ -13,6 +13,12 @@
 //                       state: h[s] = O[s, path[s, L[s]]].
 // Both are byte copies in 16-byte units; sequences whose seq_len, L or path
 // are out of range are left untouched.
+//
+// accept_tally_kernel counts, over the steps of a run, how often each (depth,
+// rank) candidate was offered (its parent lay on the accepted path) and
+// accepted: the per-rank acceptance rates from which the tree budget is
+// planned (aicassindra.com "Medusa deep dive", "From top-k heads to a sparse
+// candidate tree": the tree shape is a tuned budget).
 
 #include "common.h"
 #include "kernels.h"
@@ -53,6 +59,44 @@ __global__ __launch_bounds__(256) void next_hidden_kernel(const uint8_t* __restr
   const uint4* src = reinterpret_cast<const uint4*>(O + ((int64_t)s * T + node) * row_bytes);
   uint4* dst = reinterpret_cast<uint4*>(h + (int64_t)s * row_bytes);
   for (int u = threadIdx.x; u < row_bytes / 16; u += blockDim.x) dst[u] = src[u];
+}
+
+// One workgroup per sequence, one thread per tree node.  onpath[n] = the depth
+// at which node n lies on the accepted path (-1 if it does not); a node of
+// depth D was offered when its parent lies on the path at depth D-1, and
+// accepted when it lies on the path itself.  Counts are [K][16] (depth-1,
+// rank), added to.
+__global__ __launch_bounds__(kMaxT) void accept_tally_kernel(const int* __restrict__ L,
+                                                             const int* __restrict__ path, int K,
+                                                             TreeDev t,
+                                                             unsigned long long* __restrict__ acc,
+                                                             unsigned long long* __restrict__ off) {
+  const int s = blockIdx.x, tid = threadIdx.x;
+  __shared__ int onpath[kMaxT];
+  const int l = L[s];
+  if (l < 0 || l > K) return;            // uniform across the workgroup
+  onpath[tid] = -1;
+  __syncthreads();
+  if (tid <= l) {
+    const int n = path[(int64_t)s * (K + 1) + tid];
+    if (n >= 0 && n < t.T) onpath[n] = tid;
+  }
+  __syncthreads();
+  if (tid >= 1 && tid < t.T) {
+    const int D = t.depth[tid], r = t.rank[tid];
+    if (onpath[t.parent[tid]] == D - 1) {
+      atomicAdd(&off[(D - 1) * 16 + r], 1ull);
+      if (onpath[tid] == D) atomicAdd(&acc[(D - 1) * 16 + r], 1ull);
+    }
+  }
+}
+
+hipError_t run_accept_tally(const int* L, const int* path, int b, int K, const TreeDev& t,
+                            int64_t* accepted, int64_t* offered, hipStream_t st) {
+  hipLaunchKernelGGL(accept_tally_kernel, dim3(b), dim3(kMaxT), 0, st, L, path, K, t,
+                     reinterpret_cast<unsigned long long*>(accepted),
+                     reinterpret_cast<unsigned long long*>(offered));
+  return hipGetLastError();
 }
 
 hipError_t run_kv_append(void* Kc, void* Vc, const int* seq_len, const void* Knew,

@@ -11,6 +11,9 @@
 // they are clearly apart, otherwise by cross-multiplied big integers, so ties
 // at the cut-off (common: scores are ratios of small integers) are resolved by
 // the stated order and not by rounding.
+// Two more ways to a tree: the N candidates of largest acceptance product
+// under measured per-rank rates (plan_from_rates), and caller-given node
+// tables, validated (plan_from_tables).
 
 #include <algorithm>
 #include <cmath>
@@ -56,7 +59,8 @@ int cmp(const Big& a, const Big& b) {
 struct Cand {
   uint8_t D;
   uint8_t r[kPlanMaxDepth];
-  double logscore;
+  double logscore;   // fixed rule: log of the score
+  double score;      // rates rule: the score itself
 };
 
 struct Ranker {
@@ -100,6 +104,36 @@ std::string key_of(const int* k, int K, int N, int dn, int dd) {
 
 std::mutex g_mu;
 std::map<std::string, std::shared_ptr<const TreePlanHost>> g_cache;
+
+// Node tables of a kept candidate set: root first, then by depth and rank
+// tuple (so a parent precedes its children); nullptr if the set is not closed
+// under taking ancestors.
+std::shared_ptr<TreePlanHost> tables_of(std::vector<Cand>& kept, std::string* err) {
+  std::sort(kept.begin(), kept.end(), tuple_less);
+  auto plan = std::make_shared<TreePlanHost>();
+  const int T = (int)kept.size() + 1;
+  plan->T = T;
+  plan->parent.assign(T, -1);
+  plan->depth.assign(T, 0);
+  plan->rank.assign(T, -1);
+  std::map<std::vector<int>, int> index;
+  index[{}] = 0;
+  for (int i = 1; i < T; ++i) {
+    const Cand& c = kept[i - 1];
+    std::vector<int> t(c.r, c.r + c.D);
+    index[t] = i;
+    std::vector<int> par(t.begin(), t.end() - 1);
+    auto it = index.find(par);
+    if (it == index.end()) {
+      *err = "tree: kept set is not closed under ancestors";
+      return nullptr;
+    }
+    plan->parent[i] = it->second;
+    plan->depth[i] = c.D;
+    plan->rank[i] = c.r[c.D - 1];
+  }
+  return plan;
+}
 
 }  // namespace
 
@@ -160,34 +194,118 @@ std::shared_ptr<const TreePlanHost> get_tree_plan(const int* k, int K, int N, in
     std::sort(all.begin(), all.end(), [&](const Cand& a, const Cand& b) { return rk.before(a, b); });
     all.resize((size_t)keep);
   }
-  std::sort(all.begin(), all.end(), tuple_less);
-
-  auto plan = std::make_shared<TreePlanHost>();
-  const int T = (int)keep + 1;
-  plan->T = T;
-  plan->parent.assign(T, -1);
-  plan->depth.assign(T, 0);
-  plan->rank.assign(T, -1);
-  std::map<std::vector<int>, int> index;
-  index[{}] = 0;
-  for (int i = 1; i < T; ++i) {
-    const Cand& c = all[i - 1];
-    std::vector<int> t(c.r, c.r + c.D);
-    index[t] = i;
-    std::vector<int> par(t.begin(), t.end() - 1);
-    auto it = index.find(par);
-    if (it == index.end()) {   // cannot happen for decay < 1 (ancestor-closed)
-      *err = "tree: kept set is not closed under ancestors";
-      return nullptr;
-    }
-    plan->parent[i] = it->second;
-    plan->depth[i] = c.D;
-    plan->rank[i] = c.r[c.D - 1];
-  }
+  auto plan = tables_of(all, err);
+  if (!plan) return nullptr;
   std::lock_guard<std::mutex> g(g_mu);
   auto it = g_cache.find(key);
   if (it != g_cache.end()) return it->second;
   g_cache[key] = plan;
+  return plan;
+}
+
+// aicassindra.com "Medusa deep dive", "From top-k heads to a sparse candidate
+// tree" (the tree shape is a tuned budget) and "What it costs on a CPU-bound
+// SLM" (expected acceptance length multiplies throughput).  Candidate
+// (r_1..r_D) scores q[0][r_1] * q[1][r_2] * ... (float64, from depth 1 down):
+// the probability that its path is accepted when heads are independent given
+// the hidden state.  The N best under (score desc, D asc, tuple asc) are kept;
+// q <= 1 keeps a child's score at or below its parent's, so the kept set is
+// closed under ancestors.  Expected tokens = 1 + the kept scores summed in node
+// order.  Not cached (rates change as they are measured).
+std::shared_ptr<const TreePlanHost> plan_from_rates(const int* k, int K, int N, const double* q,
+                                                    double* expected, std::string* err) {
+  const int64_t total = full_tree_candidates(k, K);
+  if (total < 0 || total > kPlanMaxCandidates) {
+    *err = "tree: too many candidate tuples to rank (" + std::to_string(total) + ")";
+    return nullptr;
+  }
+  const int64_t keep = N < 0 ? total : N;
+  if (keep > total) {
+    *err = "tree: N exceeds the number of candidate tuples";
+    return nullptr;
+  }
+  if (keep + 1 > kPlanMaxT) {
+    *err = "tree: N + 1 exceeds the node limit";
+    return nullptr;
+  }
+  std::vector<Cand> all;
+  all.reserve((size_t)total);
+  for (int D = 1; D <= K; ++D) {
+    Cand c{};
+    c.D = (uint8_t)D;
+    std::vector<int> r(D, 0);
+    while (true) {
+      double sc = 1.0;
+      for (int d = 0; d < D; ++d) {
+        c.r[d] = (uint8_t)r[d];
+        sc = sc * q[d * kPlanRankCols + r[d]];
+      }
+      c.score = sc;
+      all.push_back(c);
+      int d = D - 1;
+      while (d >= 0 && ++r[d] == k[d]) r[d--] = 0;
+      if (d < 0) break;
+    }
+  }
+  if (keep < total) {
+    std::sort(all.begin(), all.end(), [](const Cand& a, const Cand& b) {
+      if (a.score != b.score) return a.score > b.score;
+      return tuple_less(a, b);
+    });
+    all.resize((size_t)keep);
+  }
+  auto plan = tables_of(all, err);
+  if (!plan) return nullptr;
+  // expected tokens in node order (the root contributes the 1)
+  double e = 1.0;
+  std::vector<double> node_score(plan->T, 1.0);
+  for (int i = 1; i < plan->T; ++i) {
+    node_score[i] = node_score[plan->parent[i]] * q[(plan->depth[i] - 1) * kPlanRankCols + plan->rank[i]];
+    e = e + node_score[i];
+  }
+  if (expected) *expected = e;
+  return plan;
+}
+
+std::shared_ptr<const TreePlanHost> plan_from_tables(const int* k, int K, const int* parent,
+                                                     const int* rank, int T, std::string* err) {
+  if (T < 1 || T > kPlanMaxT) {
+    *err = "tree: T must be in [1, 256]";
+    return nullptr;
+  }
+  if (parent[0] != -1) {
+    *err = "tree: node 0 must be the root (parent -1)";
+    return nullptr;
+  }
+  auto plan = std::make_shared<TreePlanHost>();
+  plan->T = T;
+  plan->parent.assign(T, -1);
+  plan->depth.assign(T, 0);
+  plan->rank.assign(T, -1);
+  std::vector<uint32_t> seen((size_t)T * 16, 0);   // (parent, rank) taken
+  for (int i = 1; i < T; ++i) {
+    const int p = parent[i], r = rank[i];
+    if (p < 0 || p >= i) {
+      *err = "tree: parent[i] must lie in [0, i)";
+      return nullptr;
+    }
+    const int D = plan->depth[p] + 1;
+    if (D > K || r < 0 || r >= k[D - 1]) {
+      *err = "tree: node deeper than K or rank outside the head's shortlist";
+      return nullptr;
+    }
+    if (D < plan->depth[i - 1]) {
+      *err = "tree: depths must not decrease along the node order";
+      return nullptr;
+    }
+    if (seen[(size_t)p * 16 + r]++) {
+      *err = "tree: two children of one node share a rank";
+      return nullptr;
+    }
+    plan->parent[i] = p;
+    plan->depth[i] = D;
+    plan->rank[i] = r;
+  }
   return plan;
 }
 

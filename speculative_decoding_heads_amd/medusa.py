@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmedusa.so")
 F32, BF16 = 0, 1
 GREEDY, TYPICAL = 0, 1
 ROOT_GIVEN = 2          # root_mode only: root[] is an input
+MAX_K = 16              # shortlist size per head at most (columns of a rate table)
 MAX_T = 256
 
 _lib = None
@@ -65,6 +66,10 @@ _SIGS = {
     "medusa_verify_logits": ([_P, _I64, _I32, _P, _I32, _I32, _I32, _F, _P, _P, _SZ, _P], _I32),
     "medusa_kv_append": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
     "medusa_next_hidden": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "medusa_tree_plan_rates": ([_P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P], _I32),
+    "medusa_topk_tree_tables": ([_P, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _F, _U64, _U64,
+                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P], _I32),
+    "medusa_accept_tally": ([_P, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -240,6 +245,38 @@ def medusa_tree_plan(k, N, decay_num=4, decay_den=5):
     return list(par), list(dep), list(rk)
 
 
+def _rates_host(k, q):
+    """q: K rows of per-rank rates (sequences or a [K, >=k_d] array) -> f64 [K][16]."""
+    K = len(k)
+    _need(len(q) == K, "q: expected one row of rates per head")
+    buf = (ctypes.c_double * (K * MAX_K))()
+    for d in range(K):
+        row = [float(x) for x in q[d]]
+        _need(len(row) >= k[d], "q: row d needs k[d] rates")
+        for r in range(k[d]):
+            buf[d * MAX_K + r] = row[r]
+    return buf
+
+
+def medusa_tree_plan_rates(k, N, q):
+    """Host-only: (parent, depth, rank, expected tokens) of the N-candidate tree
+    with the largest path acceptance products under per-rank rates q."""
+    kk = _i32_host(k)
+    qq = _rates_host(k, q)
+    T = ctypes.c_int32(0)
+    e = ctypes.c_double(0.0)
+    NN = -1 if N is None else N
+    st = lib().medusa_tree_plan_rates(kk, len(k), NN, qq, None, None, None, 0, ctypes.byref(T),
+                                      ctypes.byref(e))
+    _check("medusa_tree_plan_rates", st)
+    n = T.value
+    par, dep, rk = (ctypes.c_int32 * n)(), (ctypes.c_int32 * n)(), (ctypes.c_int32 * n)()
+    st = lib().medusa_tree_plan_rates(kk, len(k), NN, qq, par, dep, rk, n, ctypes.byref(T),
+                                      ctypes.byref(e))
+    _check("medusa_tree_plan_rates", st)
+    return list(par), list(dep), list(rk), e.value
+
+
 def medusa_build_tree(k, N, decay_num, decay_den, root, idx, seq_len, tokens, pos, parent, depth,
                       anc, stream=None):
     b, K, kmax = idx.shape
@@ -329,6 +366,43 @@ def medusa_topk_tree(logits, k, kmax, N, decay_num, decay_den, root_mode, temper
                                 _ptr(anc), anc.shape[1], _ptr(ws), 0 if ws is None else ws.numel(),
                                 _stream(stream))
     _check("medusa_topk_tree", st)
+
+
+def medusa_topk_tree_tables(logits, k, kmax, plan_parent, plan_rank, root_mode, temperature, seed,
+                            step, seq_len, root, idx, val, tokens, pos, parent, depth, anc, ws,
+                            stream=None):
+    """medusa_topk_tree for a tree given by host tables (plan_parent, plan_rank)."""
+    b, K1, V = logits.shape
+    T = len(plan_parent)
+    _need(len(plan_rank) == T, "plan_rank: expected one rank per node")
+    _topk_shapes(logits, k, kmax, root, idx, val)
+    _tree_shapes(T, b, seq_len, tokens, pos, parent, depth, anc)
+    st = lib().medusa_topk_tree_tables(_ptr(logits), b, K1 - 1, V, _i32_host(k), kmax,
+                                       _i32_host(plan_parent), _i32_host(plan_rank), T, root_mode,
+                                       temperature, seed, step, _ptr(seq_len), _ptr(root), _ptr(idx),
+                                       _ptr(val), _ptr(tokens), _ptr(pos), _ptr(parent),
+                                       _ptr(depth), _ptr(anc), anc.shape[1], _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(stream))
+    _check("medusa_topk_tree_tables", st)
+
+
+def medusa_accept_tally(L, path, k, plan_parent, plan_rank, accepted, offered, stream=None):
+    """Add one batch of steps to accepted / offered [K, 16] int64 (device)."""
+    b = L.shape[0]
+    K = len(k)
+    T = len(plan_parent)
+    _need(len(plan_rank) == T, "plan_rank: expected one rank per node")
+    _shape(L, (b,), "L")
+    _shape(path, (b, K + 1), "path")
+    _dt(L, torch.int32, "L")
+    _dt(path, torch.int32, "path")
+    for t, n in ((accepted, "accepted"), (offered, "offered")):
+        _shape(t, (K, MAX_K), n)
+        _dt(t, torch.int64, n)
+    st = lib().medusa_accept_tally(_ptr(L), _ptr(path), b, _i32_host(k), K,
+                                   _i32_host(plan_parent), _i32_host(plan_rank), T,
+                                   _ptr(accepted), _ptr(offered), _stream(stream))
+    _check("medusa_accept_tally", st)
 
 
 def medusa_accept_compact(base_logits, tokens, parent, depth, K, mode, temperature, eps, delta,

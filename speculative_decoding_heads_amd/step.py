@@ -24,8 +24,17 @@ from . import medusa as M
 
 
 class VerifyStep:
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", plan=None):
+        """plan: optional host tables (parent, rank) of the tree, e.g. from
+        medusa_tree_plan_rates (the tree budget); default: the fixed tree of
+        cfg.N candidates.  Either way the tree has cfg.T nodes."""
         self.cfg = c = cfg
+        if plan is not None:
+            parent, rank = list(plan[0]), list(plan[1])
+            if len(parent) != c.T or len(rank) != c.T:
+                raise ValueError(f"plan: expected {c.T} nodes, got {len(parent)}")
+            plan = (parent, rank)
+        self.plan = plan
         self.device = device
         dt = M.BF16 if c.dtype == "bf16" else M.F32
         self.dt = dt
@@ -67,14 +76,21 @@ class VerifyStep:
         c = self.cfg
         M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
                        stream=stream)
-        if fused:
+        root_mode = M.ROOT_GIVEN if root_given else self.mode
+        root = self.bonus if root_given else self.root
+        if fused and self.plan is not None:
+            M.medusa_topk_tree_tables(self.logits, c.k, c.kmax, self.plan[0], self.plan[1],
+                                      root_mode, c.temperature, c.seed, step, x["seq_len"], root,
+                                      self.idx, self.val, self.tokens, self.pos, self.parent,
+                                      self.depth, self.anc, self.ws_topk, stream=stream)
+        elif fused:
             M.medusa_topk_tree(self.logits, c.k, c.kmax, self.N, c.decay.numerator,
-                               c.decay.denominator, M.ROOT_GIVEN if root_given else self.mode,
-                               c.temperature, c.seed, step, x["seq_len"],
-                               self.bonus if root_given else self.root, self.idx, self.val,
-                               self.tokens, self.pos, self.parent, self.depth, self.anc,
-                               self.ws_topk, stream=stream)
+                               c.decay.denominator, root_mode, c.temperature, c.seed, step,
+                               x["seq_len"], root, self.idx, self.val, self.tokens, self.pos,
+                               self.parent, self.depth, self.anc, self.ws_topk, stream=stream)
         else:
+            if self.plan is not None:
+                raise ValueError("a given tree plan needs the fused path")
             M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step,
                           self.root, self.idx, self.val, self.ws_topk, stream=stream)
             M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
@@ -113,9 +129,9 @@ class VerifyLoop:
     Every call only enqueues kernels, so ``run`` can be captured in a HIP
     graph (``capture``) and replayed."""
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", plan=None):
         self.cfg = cfg
-        self.step = VerifyStep(cfg, device)
+        self.step = VerifyStep(cfg, device, plan)
 
     def run(self, x, Qs, Kn, Vn, step0=0, root_given_first=False, stream=None, after_step=None):
         """x: h, W, LM, Kc, Vc, seq_len (state, updated in place); Qs [S, b, T, nq, d],

@@ -175,3 +175,65 @@ def test_binding_rejects_mismatched_shapes():
                         torch.zeros(5, **i32), 2, M.GREEDY, 1.0, 0.3, 0.09, 0, 0,
                         torch.zeros(1, **i32), torch.zeros(1, 2, **i32), torch.zeros(1, 3, **i32),
                         torch.zeros(1, **i32), None)
+
+
+# ------------------------------------------------------------------ tree budget
+@pytest.mark.parametrize("k,N,seed", [((10, 10, 10, 10), 64, 1), ((3, 2, 2), 5, 2), ((4, 3), None, 3),
+                                      ((16, 16, 16), 255, 4), ((2, 2, 2), 0, 5), ((5,), 5, 6)])
+def test_tree_plan_rates_equals_oracle(k, N, seed):
+    import numpy as np
+    from oracle import tree_plan_rates
+    rng = np.random.default_rng(seed)
+    q = rng.random((len(k), 16))
+    q[:, ::3] = 0.5                      # repeated rates: ties resolved by depth, then tuple
+    q[0, 1] = 1.0
+    if len(k) > 1:
+        q[1, 0] = 0.0
+    par, dep, rk, e = M.medusa_tree_plan_rates(k, N, q)
+    plan, e_ref = tree_plan_rates(k, N, q)
+    assert par == list(plan.parent) and dep == list(plan.depth)
+    assert rk == [-1] + [t[-1] for t in plan.tuples[1:]]
+    assert e == e_ref                    # same float64 products and sums, same order
+
+
+def test_tree_budget_argument_checks():
+    L = M.lib()
+    k = M._i32_host([2, 2])
+    q = (ctypes.c_double * 32)(*([0.5] * 32))
+    T = ctypes.c_int32(0)
+    e = ctypes.c_double(0)
+    assert L.medusa_tree_plan_rates(k, 2, 3, q, None, None, None, 0, ctypes.byref(T), ctypes.byref(e)) == 0
+    assert T.value == 4 and e.value == 2.25     # (0), (1), (0,0): 1 + 0.5 + 0.5 + 0.25
+    q[1] = 1.5
+    assert L.medusa_tree_plan_rates(k, 2, 3, q, None, None, None, 0, None, None) == ERR_ARG
+    q[1] = float("nan")
+    assert L.medusa_tree_plan_rates(k, 2, 3, q, None, None, None, 0, None, None) == ERR_ARG
+    q[1] = 0.5
+    q[2] = 7.0                           # past k_0: ignored
+    assert L.medusa_tree_plan_rates(k, 2, 3, q, None, None, None, 0, None, None) == 0
+    assert L.medusa_tree_plan_rates(k, 2, 7, q, None, None, None, 0, None, None) == ERR_ARG
+    assert L.medusa_tree_plan_rates(k, 2, -2, q, None, None, None, 0, None, None) == ERR_ARG
+    assert L.medusa_tree_plan_rates(k, 2, 3, None, None, None, None, 0, None, None) == ERR_ARG
+    k16 = M._i32_host([16, 16, 16])
+    q16 = (ctypes.c_double * 48)(*([0.5] * 48))
+    assert L.medusa_tree_plan_rates(k16, 3, 256, q16, None, None, None, 0, None, None) == ERR_UNSUPPORTED
+    # explicit tables: invalid trees are rejected before anything is launched
+    fake = ctypes.c_void_p(0x1000)
+    good_p, good_r = M._i32_host([-1, 0, 0, 1]), M._i32_host([-1, 0, 1, 1])
+    for par, rk in (([-1, 0, 2, 1], [-1, 0, 1, 0]),     # parent after node
+                    ([-1, 0, 0], [-1, 0, 2]),           # rank >= k
+                    ([-1, 0, 0], [-1, 1, 1]),           # two children, one rank
+                    ([-1, 0, 1, 0], [-1, 0, 0, 1]),     # depth decreases
+                    ([0, 0], [-1, 0])):                 # node 0 not a root
+        pp, rr = M._i32_host(par), M._i32_host(rk)
+        assert L.medusa_accept_tally(fake, fake, 1, k, 2, pp, rr, len(par), fake, fake, None) == ERR_ARG
+        assert L.medusa_topk_tree_tables(fake, 1, 2, 100, k, 2, pp, rr, len(par), M.GREEDY, 1.0, 0, 0,
+                                         fake, fake, fake, fake, fake, fake, fake, fake, fake, 1,
+                                         fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_accept_tally(fake, fake, 1, k, 2, good_p, good_r, 4, fake,
+                                 ctypes.c_void_p(0x1004), None) == ERR_ARG      # misaligned counts
+    assert L.medusa_accept_tally(None, None, 0, k, 2, good_p, good_r, 4, None, None, None) == 0
+    assert L.medusa_accept_tally(fake, fake, 1, k, 2, None, good_r, 4, fake, fake, None) == ERR_ARG
+    assert L.medusa_topk_tree_tables(fake, 1, 2, 100, k, 2, good_p, good_r, 4, M.GREEDY, 1.0, 0, 0,
+                                     fake, fake, fake, fake, fake, fake, fake, fake, fake, 0,
+                                     fake, 1 << 20, None) == ERR_ARG            # anc_words < 1
