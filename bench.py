@@ -77,9 +77,15 @@ def _enqueue(st, x, step, M, c, ev=None):
     mark(0)
     M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
     mark(1)
-    M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
-                       st.mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx, st.val,
-                       st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
+    if st.plan is not None:
+        M.medusa_topk_tree_tables(st.logits, c.k, c.kmax, st.plan[0], st.plan[1], st.mode,
+                                  c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
+                                  st.val, st.tokens, st.pos, st.parent, st.depth, st.anc,
+                                  st.ws_topk)
+    else:
+        M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
+                           st.mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
+                           st.val, st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
     mark(2)
     M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
     mark(3)
@@ -94,7 +100,7 @@ def _enqueue(st, x, step, M, c, ev=None):
     mark(5)
 
 
-def measure(cfg, steps, warmup, rotate=None, log=print):
+def measure(cfg, steps, warmup, rotate=None, log=print, plan=None):
     import torch
     from speculative_decoding_heads_amd import medusa as M
     from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
@@ -114,7 +120,7 @@ def measure(cfg, steps, warmup, rotate=None, log=print):
     del host
     log(f"[bench] {c.name}: inputs {ws_bytes / 1e6:.1f} MB x {rotate} copies "
         f"({time.time() - t0:.1f}s)")
-    st = VerifyStep(c)
+    st = VerifyStep(c, plan=plan)
     n = warmup + 2 * steps
     seqs = [torch.full((c.b,), c.P, dtype=torch.int32, device="cuda") for _ in range(n)]
 
@@ -181,6 +187,41 @@ def measure_loop(cfg, steps_per_graph, replays, warmup_replays=2, log=print):
     log(f"[bench] {c.name}: loop of {steps_per_graph} steps x {replays} graph replays, "
         f"{ms * 1e3:.1f} us per step, final seq_len {x['seq_len'].tolist()[:4]}")
     return ms
+
+
+def budget_rates(k):
+    """Per-rank acceptance rates standing in for measured ones (no trained heads
+    here): head d+1 holds the accepted token in its shortlist with probability
+    0.9 - 0.1 d, spread over the ranks geometrically (ratio 1/2).  The full
+    7B-shape tree then expects 3.43 tokens per step."""
+    q = []
+    for d, s in enumerate(k):
+        w = [0.5 ** r for r in range(s)]
+        q.append([(0.9 - 0.1 * d) * x / sum(w) for x in w])
+    return q
+
+
+def tree_sweep(cfg, sizes, steps, warmup, log=print):
+    """The tree budget on the device: for each candidate count N the tree of most
+    expected tokens under budget_rates (medusa_tree_plan_rates), its measured
+    step rate, and expected tokens per second = expected tokens x steps/s."""
+    from speculative_decoding_heads_amd import medusa as M
+    q = budget_rates(cfg.k)
+    points = []
+    for N in sizes:
+        par, _, rk, e = M.medusa_tree_plan_rates(cfg.k, N, q)
+        c = cfg.with_(N=N)
+        ms, _ = measure(c, steps, warmup, None, log, plan=(par, rk))
+        points.append({"candidates": N, "nodes": N + 1, "expected_tokens": round(e, 4),
+                       "steps_per_s": round(1000.0 / ms, 1),
+                       "tokens_per_s": round(e * 1000.0 / ms, 1)})
+        log(f"[bench] tree budget N={N}: {e:.3f} tokens/step x {1000.0 / ms:.0f} steps/s")
+    best = max(points, key=lambda p: p["tokens_per_s"])
+    return {"workload": cfg.name,
+            "rates": "synthetic stand-in: head d+1 holds the accepted token with probability "
+                     "0.9 - 0.1 d, geometric over ranks (ratio 1/2)",
+            "points": points, "best_candidates": best["candidates"],
+            "best_tokens_per_s": best["tokens_per_s"]}
 
 
 def cpu_baseline(cfg, seconds, log=print):
@@ -297,6 +338,9 @@ def main():
                     help="skip the measured copy / read / vendor-GEMM reference rates")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--tree-sweep", default="",
+                    help="comma-separated candidate counts: measure the tree budget "
+                         "(expected tokens per second per tree size) on the workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -358,6 +402,9 @@ def main():
                        "unit": "verify-steps/s", "ms_per_step": round(ms_l, 4),
                        "steps_per_graph": args.loop, "replays": args.loop_replays,
                        "hip_graph": True}
+    if args.tree_sweep:
+        sizes = [int(v) for v in args.tree_sweep.split(",") if v.strip()]
+        out["tree_sweep"] = tree_sweep(cfg, sizes, args.steps, args.warmup, log)
     torch.cuda.synchronize()
     out["measured_peaks"] = None if args.no_peaks else measured_peaks(log)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds, log)

@@ -621,7 +621,13 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
         }
       }
     p.ntiles = (N + 64 * p.wnb - 1) / (64 * p.wnb);
-    return p;
+    // Up to 160 rows the streaming kernel (8 or 10 row blocks per workgroup)
+    // beats a ring that fills less than two rounds of the 256 CUs: 32000
+    // columns at 97-160 rows took 59-74 us against 83-85 us; at 128256
+    // columns (1002 ring workgroups) the ring stays ahead.
+    const long ring_wgs = (long)((M + 32 * p.wmb - 1) / (32 * p.wmb)) * p.ntiles;
+    if (mb > 10 || ring_wgs >= 2 * 256) return p;
+    p = Bf16Plan{};
   }
   p.kind = 1;
   p.mb = mb <= 6 ? mb : mb <= 8 ? 8 : mb <= 10 ? 10 : 8;

@@ -108,7 +108,8 @@ def test_head_rows_and_base_rows_differ_only_in_summation_order(b, H, V):
                                        (5, 384, 31000), (65, 256, 30977), (16, 640, 33000),
                                        (80, 128, 30720), (5, 256, 40000), (65, 128, 50000),
                                        (16, 256, 60000), (161, 128, 40001),
-                                       (1040, 384, 3333)])
+                                       (1040, 384, 3333), (97, 256, 32000), (129, 384, 5000),
+                                       (150, 256, 31000), (160, 128, 128256)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
