@@ -32,7 +32,8 @@ from .topk import topk_stable, argmax_lowest
 from .rng import splitmix64, counter_uniform, sample_tempered
 from .tree import tree_plan, tree_gather, full_tree_node_count, full_path_count, TreePlan
 from .attention import tree_attention, path_attention
-from .accept import accept_greedy_walk, accept_greedy_parallel, accept_typical, typical_local
+from .accept import (accept_greedy_walk, accept_greedy_parallel, accept_typical, typical_local,
+                     accept_reject)
 from .compact import kv_compact
 from .step import oracle_step
 from .budget import tree_plan_rates, expected_tokens, plan_from_tables, accept_tally
@@ -42,6 +43,6 @@ __all__ = [
     "splitmix64", "counter_uniform", "sample_tempered", "tree_plan", "tree_gather",
     "full_tree_node_count", "full_path_count", "TreePlan", "tree_attention",
     "path_attention", "accept_greedy_walk", "accept_greedy_parallel",
-    "accept_typical", "typical_local", "kv_compact", "oracle_step",
+    "accept_typical", "typical_local", "accept_reject", "kv_compact", "oracle_step",
     "tree_plan_rates", "expected_tokens", "plan_from_tables", "accept_tally",
 ]

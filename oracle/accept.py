@@ -25,11 +25,29 @@ Readings:
     sample from softmax(logits / T) (typical; draw 1 of the counter sampler);
   * path = node indices root .. chosen node, padded with -1 to K+1 entries;
     accepted tokens likewise.
+
+Exact rejection sampling (accept_reject).  aiunderstanding.org "Medusa
+Decoding Heads" ("Deep Dive"): with the backbone frozen, rejection sampling
+against the original model can keep its output distribution (lossless);
+aicassindra.com "Medusa deep dive", "Typical acceptance, not exact rejection
+sampling": the heads give no clean proposal distribution to reject against.
+Reading: the candidates of a node are taken as point-mass proposals, tried in
+node order.  At node n with tempered distribution p_n = softmax(row_n / T),
+child j (token t_j) is accepted when u_j * (1 - r_j) < p_n(t_j), r_j the mass
+of the children already rejected (p_n(t_1) + ... + p_n(t_{j-1})); the walk
+moves to the first accepted child.  When every child of n is rejected, the
+next token is drawn from p_n with those children's tokens removed (inverse
+CDF on the remaining mass, draw 1); when n has no children, from p_n itself.
+Each emitted token is then distributed exactly as p at its position: child j
+is emitted with probability p(t_j) and the residual covers the rest.  Draws:
+u_j of the child at index j among the children of a depth-d node is draw
+16 d + j of the counter sampler keyed by splitmix64(seed) (separate from the
+root and bonus draws keyed by seed).
 """
 
 import numpy as np
 
-from .rng import counter_uniform, sample_tempered
+from .rng import counter_uniform, sample_tempered, splitmix64
 
 
 def _path_to(best, parent, K):
@@ -133,3 +151,52 @@ def accept_typical(base_logits, tokens, parent, depth, K, temperature, eps, delt
     u = counter_uniform(seed, step, seq, 1)
     bonus, _ = sample_tempered(base_logits[best], temperature, u)
     return L, path, acc, bonus, margins
+
+
+def accept_reject(base_logits, tokens, parent, K, temperature, seed, step, seq):
+    """Exact rejection sampling over the tree for one sequence.
+
+    Returns (L, path, acc_tokens, bonus, margins): margins lists, for every
+    decision taken, |u (1 - r) - p| / p (near-tie accounting; inf when p = 0).
+    """
+    T = len(tokens)
+    children = [[] for _ in range(T)]
+    for c in range(1, T):
+        children[int(parent[c])].append(c)
+
+    def probs(n):
+        x = np.asarray(base_logits[n], dtype=np.float64) / float(temperature)
+        e = np.exp(x - x.max())
+        return e / e.sum()
+
+    seed_w = splitmix64(seed)
+    n, d, margins = 0, 0, []
+    rejected_all = False
+    while children[n]:
+        p = probs(n)
+        r, nxt = 0.0, None
+        for j, c in enumerate(children[n]):
+            pc = float(p[int(tokens[c])])
+            u = counter_uniform(seed_w, step, seq, 16 * d + j)
+            lhs = u * (1.0 - r)
+            margins.append(abs(lhs - pc) / pc if pc > 0 else np.inf)
+            if lhs < pc:
+                nxt = c
+                break
+            r += pc
+        if nxt is None:
+            rejected_all = True
+            break
+        n, d = nxt, d + 1
+    L = d
+    path = _path_to(n, parent, K)
+    acc = np.array([int(tokens[i]) if i >= 0 else -1 for i in path], dtype=np.int64)
+    x = np.asarray(base_logits[n], dtype=np.float64) / float(temperature)
+    e = np.exp(x - x.max())
+    if rejected_all:
+        for c in children[n]:
+            e[int(tokens[c])] = 0.0
+    cdf = np.cumsum(e)
+    u = counter_uniform(seed, step, seq, 1)
+    bonus = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+    return L, path, acc, min(bonus, e.size - 1), margins
