@@ -78,13 +78,13 @@ def _enqueue(st, x, step, M, c, ev=None):
     M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
     mark(1)
     if st.plan is not None:
-        M.medusa_topk_tree_tables(st.logits, c.k, c.kmax, st.plan[0], st.plan[1], st.mode,
+        M.medusa_topk_tree_tables(st.logits, c.k, c.kmax, st.plan[0], st.plan[1], st.root_mode,
                                   c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
                                   st.val, st.tokens, st.pos, st.parent, st.depth, st.anc,
                                   st.ws_topk)
     else:
         M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
-                           st.mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
+                           st.root_mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
                            st.val, st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
     mark(2)
     M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)

@@ -56,6 +56,9 @@ typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_mode;
 /* root_mode of medusa_topk / medusa_topk_tree only: root[] is an input (the
  * previous step's next token, see medusa_next_hidden). */
 #define MEDUSA_ROOT_GIVEN 2
+/* mode of medusa_accept / medusa_accept_compact / medusa_verify_logits only:
+ * exact rejection sampling over the tree (see medusa_accept). */
+#define MEDUSA_REJECT 3
 
 /* Limits of this build. */
 #define MEDUSA_MAX_HEADS 16     /* Medusa heads K */
@@ -222,6 +225,21 @@ int medusa_tree_attn(const void* Q, const void* Kc, const void* Vc, const int32_
  *   bonus [b]           next token at the chosen node: argmax (GREEDY) or a
  *                       float64 sample from softmax(x / temperature) with
  *                       counter draw 1 (TYPICAL; same rule as medusa_topk)
+ *   REJECT (exact rejection sampling; [guide] "Deep Dive": rejection against
+ *   the original model keeps its output distribution; [deep-dive]: the heads
+ *   give no proposal distribution of their own): the candidates of a node
+ *   are point-mass proposals tried in node order.  With p = softmax(
+ *   base_logits[n] / temperature) at node n, its j-th child c (token t) is
+ *   taken when u * (1 - r) < p[t], r = the p of the children tried before it
+ *   and u = counter draw 16 * depth(n) + j keyed by splitmix64(seed); the
+ *   walk moves to the first taken child, from the root down.  L and the
+ *   chosen node are where it stops.  bonus: counter draw 1 from p at the
+ *   chosen node with its children's tokens removed (they were all
+ *   rejected), from the full p when it has none.  Every emitted token is
+ *   then distributed as p at its position.  p comes from the float32
+ *   statistics of the typical path (taken in float64), so a decision can
+ *   differ from exact arithmetic only when u * (1 - r) lies within that
+ *   rounding of p[t].  eps and delta are not used.
  * ------------------------------------------------------------------------- */
 size_t medusa_accept_workspace(int32_t b, int32_t T);
 int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t* parent,
@@ -272,7 +290,7 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
  * (n_heads = 0, include_base = 1: logits [rows, V] f32 = x [rows, H] . LM^T)
  * that also leaves, in ws, the acceptance statistics of every row per weight
  * tile: the argmax key (GREEDY) or the online softmax statistics of
- * logits / temperature (TYPICAL).  medusa_accept_compact consumes them
+ * logits / temperature (TYPICAL and REJECT).  medusa_accept_compact consumes them
  * (verify_ws), so acceptance does not re-read the logits.  Below 2^24 logits
  * (rows * V) re-reading is cheaper: then no partials are kept and
  * medusa_accept_compact reads the logits as without verify_ws.  [glossary]

@@ -20,7 +20,7 @@ from .topk import topk_stable, argmax_lowest
 from .rng import counter_uniform, sample_tempered
 from .tree import tree_plan, tree_gather
 from .attention import tree_attention
-from .accept import accept_greedy_walk, accept_greedy_parallel, accept_typical
+from .accept import accept_greedy_walk, accept_greedy_parallel, accept_typical, accept_reject
 from .compact import kv_compact
 
 
@@ -63,10 +63,15 @@ def oracle_step(h, W, LM, Q, Kc, Vc, P, k, N, decay, mode, bf16,
                 base_logits[s], tokens[s], plan.parent, K)
             chk = accept_greedy_parallel(base_logits[s], tokens[s], plan.parent, plan.depth, K)
             assert chk[0] == L[s] and (chk[1] == path[s]).all() and chk[3] == bonus[s]
-        else:
+        elif mode == "typical":
             L[s], path[s], acc[s], bonus[s], _ = accept_typical(
                 base_logits[s], tokens[s], plan.parent, plan.depth, K,
                 temperature, eps, delta, seed, step, s)
+        elif mode == "reject":
+            L[s], path[s], acc[s], bonus[s], _ = accept_reject(
+                base_logits[s], tokens[s], plan.parent, K, temperature, seed, step, s)
+        else:
+            raise ValueError(f"unknown acceptance mode {mode!r}")
         Kn[s], Vn[s], new_len[s] = kv_compact(Kc[s], Vc[s], int(P[s]), path[s], int(L[s]))
     return dict(u=u, logits=logits, root=root, idx=idx, plan=plan, tokens=tokens,
                 pos=pos, O=O, base_logits=base_logits, L=L, path=path,

@@ -24,7 +24,7 @@ class Config:
     d: int                     # head dim
     P: int                     # prefix length per sequence
     dtype: str                 # "f32" or "bf16" (logits are always fp32)
-    mode: str                  # "greedy" or "typical"
+    mode: str                  # "greedy", "typical" or "reject"
     temperature: float = 0.7
     eps: float = 0.3
     delta: float = 0.09

@@ -1,4 +1,5 @@
-// Greedy / typical acceptance, path choice and the next token.
+// Greedy / typical / exact rejection-sampling acceptance, path choice and the
+// next token.
 //
 // aiunderstanding.org "Medusa Decoding Heads" ("Deep Dive"): accept the longest
 // prefix that matches what the model would have produced; inferensys.com
@@ -27,6 +28,17 @@
 //     walking ancestors, block max/min for L and the chosen node, path and
 //     accepted tokens.
 //   typical mode then runs the shared float64 row sampler on the chosen node.
+//
+// Rejection mode (aiunderstanding.org "Medusa Decoding Heads", "Deep Dive":
+// rejection sampling against the original model keeps its distribution;
+// aicassindra.com "Medusa deep dive": the heads give no proposal distribution
+// of their own): a node's candidates are point-mass proposals tried in node
+// order; child j is taken when u_j (1 - r_j) < p(t_j) (r_j = the mass of the
+// children already rejected, p the parent's tempered distribution from the
+// typical statistics), so every candidate is emitted with exactly its
+// probability.  The walk follows the first taken child; where every child is
+// rejected the next token is drawn from the row without those children's
+// tokens (the sampler's exclusion list), at a leaf from the full row.
 
 #include "common.h"
 #include "compact_dev.h"
@@ -175,7 +187,9 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
                                                    int* __restrict__ bonus, int* __restrict__ best_out,
                                                    uint8_t* __restrict__ Kc, uint8_t* __restrict__ Vc,
                                                    int* __restrict__ seq_len, int nkv, int Pmax,
-                                                   int row_bytes) {
+                                                   int row_bytes, uint64_t seed, uint64_t step,
+                                                   int* __restrict__ excl) {
+  constexpr bool kStats = MODE == kTypical || MODE == kReject;   // tempered row statistics
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ int spath[kMaxHeads + 1];
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
     sdepth[tid] = depth[tid];
     stok[tid] = my_tok;
     my_valid = tid > 0 && my_tok >= 0 && my_tok < V && my_parent >= 0 && my_parent < tid;
-    if (MODE == kTypical && my_valid)
+    if (kStats && my_valid)
       my_logit = logits[((int64_t)s * T + my_parent) * V + my_tok];
   }
   // per-node statistics of this sequence
@@ -210,31 +224,88 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
     else sstat[p] = stats[row];
   }
   __syncthreads();
-  if (tid < T) {
-    bool ok = tid == 0;
-    if (my_valid) {
-      if (MODE == kGreedy) {
-        ok = my_tok == samax[my_parent];
-      } else {
+  if constexpr (MODE == kReject) {
+    // Exact rejection sampling: p = the node's token under its parent's
+    // tempered distribution; child j (node order) of a depth-d node is
+    // accepted when u * (1 - r) < p, r = the p of its earlier siblings, u =
+    // draw 16 d + j keyed by splitmix64(seed); the walk takes the first
+    // accepted child at every node.
+    __shared__ double sp[kMaxT];
+    __shared__ int first_acc[kMaxT];
+    if (tid < T) {
+      double pc = 0.0;
+      if (my_valid) {
         const RowStat st = sstat[my_parent];
-        const double lns = log((double)st.s);
-        const double H = lns - (double)st.t / (double)st.s;
-        const double logq = (double)(my_logit * inv_temp) - (double)st.m - lns;
-        const double thr = fmin((double)eps, (double)delta * exp(-H));
-        ok = exp(logq) > thr;
+        pc = exp((double)(my_logit * inv_temp) - (double)st.m - log((double)st.s));
       }
+      sp[tid] = pc;
+      first_acc[tid] = T;
     }
-    local[tid] = ok;
-  }
-  __syncthreads();
-  // A parent table is valid when 0 <= parent[c] < c; anything else is treated
-  // as a rejected node, so the walks below always end.
-  for (int c = tid; c < T; c += blockDim.x) {
-    if (full_path(c, sparent, local)) atomicMax(&bestL, sdepth[c]);
-  }
-  __syncthreads();
-  for (int c = tid; c < T; c += blockDim.x) {
-    if (full_path(c, sparent, local) && sdepth[c] == bestL) atomicMin(&bestNode, c);
+    __syncthreads();
+    if (tid < T && my_valid) {
+      double r = 0.0;
+      int j = 0;
+      for (int c = 1; c < tid; ++c)
+        if (sparent[c] == my_parent) {
+          r += sp[c];
+          ++j;
+        }
+      const uint64_t draw = (uint64_t)(16 * sdepth[my_parent] + j);
+      const double u = counter_uniform(splitmix64(seed), step, (uint64_t)s, draw);
+      if (u * (1.0 - r) < sp[tid]) atomicMin(&first_acc[my_parent], tid);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int n = 0, d = 0;
+      while (d < K && first_acc[n] < T) {   // children follow their parent: the walk ends
+        n = first_acc[n];
+        ++d;
+      }
+      bestL = d;
+      bestNode = n;
+    }
+    __syncthreads();
+    // the stop node's children were all rejected: the next token is drawn
+    // without their tokens (none when it has no children)
+    if (tid < kSampExcl) {
+      int cnt = 0, tok = -1;
+      for (int c = 1; c < T; ++c)
+        if (sparent[c] == bestNode) {
+          if (cnt == tid) {
+            tok = stok[c];
+            break;
+          }
+          ++cnt;
+        }
+      excl[(int64_t)s * kSampExcl + tid] = tok;
+    }
+  } else {
+    if (tid < T) {
+      bool ok = tid == 0;
+      if (my_valid) {
+        if (MODE == kGreedy) {
+          ok = my_tok == samax[my_parent];
+        } else {
+          const RowStat st = sstat[my_parent];
+          const double lns = log((double)st.s);
+          const double H = lns - (double)st.t / (double)st.s;
+          const double logq = (double)(my_logit * inv_temp) - (double)st.m - lns;
+          const double thr = fmin((double)eps, (double)delta * exp(-H));
+          ok = exp(logq) > thr;
+        }
+      }
+      local[tid] = ok;
+    }
+    __syncthreads();
+    // A parent table is valid when 0 <= parent[c] < c; anything else is
+    // treated as a rejected node, so the walks below always end.
+    for (int c = tid; c < T; c += blockDim.x) {
+      if (full_path(c, sparent, local)) atomicMax(&bestL, sdepth[c]);
+    }
+    __syncthreads();
+    for (int c = tid; c < T; c += blockDim.x) {
+      if (full_path(c, sparent, local) && sdepth[c] == bestL) atomicMin(&bestNode, c);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -265,10 +336,12 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
 }
 
 // Workspace: stats per node row, amax per node row, the chosen node per
-// sequence, then (16-byte aligned) the sampler's slice partials.
+// sequence, the excluded tokens per sequence (rejection mode), then (16-byte
+// aligned) the sampler's slice partials.
 static size_t samp_offset(int b, int T) {
   const size_t rows = (size_t)b * T;
-  return (rows * sizeof(RowStat) + rows * sizeof(int) + (size_t)b * sizeof(int) + 15) & ~(size_t)15;
+  return (rows * sizeof(RowStat) + rows * sizeof(int) + (size_t)b * sizeof(int) +
+          (size_t)b * kSampExcl * sizeof(int) + 15) & ~(size_t)15;
 }
 
 size_t accept_workspace(int b, int T) { return samp_offset(b, T) + sample_workspace(b); }
@@ -282,6 +355,7 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   RowStat* stats = static_cast<RowStat*>(ws);
   int* amax = reinterpret_cast<int*>(stats + rows);
   int* best = amax + rows;
+  int* excl = best + b;
   const float inv_temp = 1.0f / temperature;
   uint8_t* Kc = kv ? static_cast<uint8_t*>(kv->Kc) : nullptr;
   uint8_t* Vc = kv ? static_cast<uint8_t*>(kv->Vc) : nullptr;
@@ -303,22 +377,32 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
                          base_logits, V, inv_temp, amax, stats);
     hipLaunchKernelGGL(accept_walk<kGreedy>, dim3(b), dim3(256), 0, st, base_logits, tokens,
                        parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
-                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, seed, step,
+                       excl);
     return hipGetLastError();
   }
+  // typical and rejection modes: tempered statistics of every node row
   if (parts)
     hipLaunchKernelGGL(accept_parts<kTypical>, dim3(pgrid), dim3(256), 0, st, hdr, pkey, pstat,
                        (int)rows, amax, stats);
   else
     hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
                        base_logits, V, inv_temp, amax, stats);
-  hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens, parent,
-                     depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path, acc_tokens, bonus,
-                     best, Kc, Vc, seq_len, nkv, Pmax, row_bytes);
+  if (mode == kReject)
+    hipLaunchKernelGGL(accept_walk<kReject>, dim3(b), dim3(256), 0, st, base_logits, tokens,
+                       parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, seed, step,
+                       excl);
+  else
+    hipLaunchKernelGGL(accept_walk<kTypical>, dim3(b), dim3(256), 0, st, base_logits, tokens,
+                       parent, depth, T, V, K, inv_temp, eps, delta, amax, stats, L, path,
+                       acc_tokens, bonus, best, Kc, Vc, seq_len, nkv, Pmax, row_bytes, seed, step,
+                       excl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return run_sample_rows(base_logits, (int64_t)T * V, best, b, V, temperature, seed, step, 1, bonus,
-                         static_cast<char*>(ws) + samp_offset(b, T), st);
+                         static_cast<char*>(ws) + samp_offset(b, T), st, nullptr, 0,
+                         mode == kReject ? excl : nullptr);
 }
 
 }  // namespace medusa

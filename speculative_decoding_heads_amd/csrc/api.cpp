@@ -116,9 +116,10 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
 // ------------------------------------------------------------------- verify logits + partials
 size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode) {
   if (rows <= 0 || H <= 0 || V <= 0 || !dtype_ok(dtype)) return 0;
-  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL) return 0;
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_REJECT) return 0;
   if (rows > INT32_MAX / 2) return 0;
-  return round_up(verify_workspace((int)rows, V, H, dtype, mode));
+  // rejection sampling works from the same tempered statistics as typical
+  return round_up(verify_workspace((int)rows, V, H, dtype, mode == MEDUSA_GREEDY ? kGreedy : kTypical));
 }
 
 int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
@@ -127,9 +128,9 @@ int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM,
   if (rows < 0) return fail(MEDUSA_ERR_ARG, "rows < 0");
   if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
   if (H <= 0 || V <= 0) return fail(MEDUSA_ERR_ARG, "H and V must be positive");
-  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
-    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
-  if (mode == MEDUSA_TYPICAL && !(temperature > 0.f && std::isfinite(temperature)))
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_REJECT)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY, TYPICAL or REJECT");
+  if (mode != MEDUSA_GREEDY && !(temperature > 0.f && std::isfinite(temperature)))
     return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
   if (rows == 0) return MEDUSA_OK;
   if (!x || !LM || !logits) return fail(MEDUSA_ERR_ARG, "x, LM and logits must be non-NULL");
@@ -141,8 +142,9 @@ int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM,
   const size_t need = medusa_verify_workspace(rows, H, V, dtype, mode);
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "verify: workspace too small");
   if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
-  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
-  return hip_status(run_verify_logits(x, (int)rows, H, LM, V, dtype, logits, mode, tmp, ws,
+  const float tmp = mode != MEDUSA_GREEDY ? temperature : 1.0f;
+  return hip_status(run_verify_logits(x, (int)rows, H, LM, V, dtype, logits,
+                                      mode == MEDUSA_GREEDY ? kGreedy : kTypical, tmp, ws,
                                       as_stream(stream)),
                     "verify logits");
 }
@@ -388,14 +390,13 @@ int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t
   if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
   if (V < 1) return fail(MEDUSA_ERR_ARG, "V must be positive");
   if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
-  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
-    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
-  if (mode == MEDUSA_TYPICAL) {
-    if (!(temperature > 0.f && std::isfinite(temperature)))
-      return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
-    if (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta)))
-      return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
-  }
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_REJECT)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY, TYPICAL or REJECT");
+  if (mode != MEDUSA_GREEDY && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  if (mode == MEDUSA_TYPICAL &&
+      (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta))))
+    return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
   if (b == 0) return MEDUSA_OK;
   if (!base_logits || !tokens || !parent || !depth || !L || !path || !acc_tokens || !bonus)
     return fail(MEDUSA_ERR_ARG, "NULL pointer");
@@ -403,7 +404,7 @@ int medusa_accept(const float* base_logits, const int32_t* tokens, const int32_t
   const size_t need = medusa_accept_workspace(b, T);
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
   if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
-  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
+  const float tmp = mode != MEDUSA_GREEDY ? temperature : 1.0f;
   return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,
                                delta, seed, step, L, path, acc_tokens, bonus, ws,
                                as_stream(stream)),
@@ -421,14 +422,13 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
   if (b < 0 || T < 1 || T > MEDUSA_MAX_T) return fail(MEDUSA_ERR_ARG, "need b >= 0, 1 <= T <= 256");
   if (V < 1) return fail(MEDUSA_ERR_ARG, "V must be positive");
   if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
-  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL)
-    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY or TYPICAL");
-  if (mode == MEDUSA_TYPICAL) {
-    if (!(temperature > 0.f && std::isfinite(temperature)))
-      return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
-    if (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta)))
-      return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
-  }
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_REJECT)
+    return fail(MEDUSA_ERR_ARG, "mode must be GREEDY, TYPICAL or REJECT");
+  if (mode != MEDUSA_GREEDY && !(temperature > 0.f && std::isfinite(temperature)))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive and finite");
+  if (mode == MEDUSA_TYPICAL &&
+      (!(eps > 0.f && std::isfinite(eps)) || !(delta > 0.f && std::isfinite(delta))))
+    return fail(MEDUSA_ERR_ARG, "eps and delta must be positive and finite");
   if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
   if (nkv < 1 || Pmax < 1 || d < 1) return fail(MEDUSA_ERR_ARG, "bad shape");
   if ((d * elem_size(dtype)) % 16 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d * sizeof(dtype) must be a multiple of 16");
@@ -441,7 +441,7 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
   const size_t need = medusa_accept_workspace(b, T);
   if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "accept: workspace too small");
   if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "workspace must be 16-byte aligned");
-  const float tmp = mode == MEDUSA_TYPICAL ? temperature : 1.0f;
+  const float tmp = mode != MEDUSA_GREEDY ? temperature : 1.0f;
   KvRollback kv{Kc, Vc, seq_len, nkv, Pmax, d, dtype};
   const void* parts = verify_ws && verify_uses_parts((int64_t)b * T, V) ? verify_ws : nullptr;
   return hip_status(run_accept(base_logits, tokens, parent, depth, b, T, V, K, mode, tmp, eps,

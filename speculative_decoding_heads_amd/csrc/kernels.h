@@ -8,7 +8,8 @@
 namespace medusa {
 
 enum { kF32 = 0, kBF16 = 1 };
-enum { kGreedy = 0, kTypical = 1, kRootGiven = 2 };   // kRootGiven: root_mode only
+// kRootGiven: root_mode only; kReject: acceptance mode only
+enum { kGreedy = 0, kTypical = 1, kRootGiven = 2, kReject = 3 };
 
 constexpr int kMaxHeads = 16;   // Medusa heads K
 constexpr int kMaxK = 16;       // shortlist size per head
@@ -69,11 +70,12 @@ hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx,
 // The draw goes to out[s] and, if out2 is given, to out2[s * out2_stride].
 // ws: sample_workspace(b) bytes, 16-byte aligned (per-slice partial sums).
 constexpr int kSampSlices = 64;
+constexpr int kSampExcl = 16;    // tokens a draw can exclude (the children of one node)
 size_t sample_workspace(int b);
 hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
                            float temperature, uint64_t seed, uint64_t step, uint64_t draw,
                            int* out, void* ws, hipStream_t st, int* out2 = nullptr,
-                           int out2_stride = 0);
+                           int out2_stride = 0, const int* excl = nullptr);
 
 hipError_t run_build_tree(const TreeDev& t, const int* root, const int* idx, int b,
                           const int* seq_len, int* tokens, int* pos, int* parent, int* depth,

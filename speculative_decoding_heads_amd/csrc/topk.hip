@@ -333,6 +333,9 @@ hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx,
 // The running sums differ from a serial float64 sum only by rounding, so a
 // sample can differ from the serial rule only when u * sum lies within a few
 // ulps of a running sum.
+// With an exclusion list (up to kSampExcl tokens per row, -1 padded) the draw
+// is from the row with those tokens removed: their e_i leave their slices'
+// shares and the total, and the rescan skips them.
 constexpr int kSampThreads = 256;
 
 struct SampPart {
@@ -389,10 +392,12 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
                                                             uint64_t seed, uint64_t step,
                                                             uint64_t draw,
                                                             const SampPart* __restrict__ parts,
+                                                            const int* __restrict__ excl,
                                                             int* __restrict__ out,
                                                             int* __restrict__ out2,
                                                             int out2_stride) {
   static_assert(kSampSlices == 64, "one lane per slice");
+  static_assert(kSampExcl <= 64, "one lane per excluded token");
   constexpr int NW = kSampThreads / 64;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -402,11 +407,35 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   __shared__ int sh_j, found;
   __shared__ double sh_base, sh_target, sh_max;
   __shared__ double wsum[NW];
+  __shared__ int sx[kSampExcl];
 
+  if (tid < kSampExcl) {
+    const int t = excl ? excl[(int64_t)s * kSampExcl + tid] : -1;
+    sx[tid] = t >= 0 && t < V ? t : -1;
+  }
+  __syncthreads();
+  auto excluded = [&](int e) {
+    bool hit = false;
+#pragma unroll
+    for (int q = 0; q < kSampExcl; ++q) hit |= sx[q] == e;
+    return hit;
+  };
   if (wave == 0) {
     const SampPart p = parts[(int64_t)s * kSampSlices + lane];
     const double M = (double)wave_max((float)p.m);
-    const double c = p.m == -(double)INFINITY ? 0.0 : p.s * exp((p.m - M) * rt);
+    double c = p.m == -(double)INFINITY ? 0.0 : p.s * exp((p.m - M) * rt);
+    if (excl) {
+      // each excluded token's share leaves its slice (lane q holds token q)
+      const int tq = lane < kSampExcl ? sx[lane] : -1;
+      const double eq = tq >= 0 ? exp(((double)x[tq] - M) * rt) : 0.0;
+#pragma unroll
+      for (int q = 0; q < kSampExcl; ++q) {
+        const int t = __shfl(tq, q, 64);
+        const double e = __shfl(eq, q, 64);
+        if (t >= 0 && lane == t / Ls) c -= e;
+      }
+      c = fmax(c, 0.0);
+    }
     double incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -439,7 +468,8 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   const int per = (hi - lo + kSampThreads - 1) / kSampThreads;
   const int tlo = min(hi, lo + tid * per), thi = min(hi, tlo + per);
   double part = 0.0;
-  for (int e = tlo; e < thi; ++e) part += exp(((double)x[e] - md) * rt);
+  for (int e = tlo; e < thi; ++e)
+    if (!excl || !excluded(e)) part += exp(((double)x[e] - md) * rt);
   double incl = part;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -457,19 +487,26 @@ __global__ __launch_bounds__(kSampThreads) void sample_pick(const float* __restr
   const double end = b0 + (wpre + incl);
   if (tlo < thi && start <= target && end > target) {
     double run = start;
-    int pick = thi - 1;
+    int pick = -1;
     for (int e = tlo; e < thi; ++e) {
+      if (excl && excluded(e)) continue;
       run += exp(((double)x[e] - md) * rt);
-      if (run > target) {
-        pick = e;
-        break;
-      }
+      pick = e;
+      if (run > target) break;
     }
-    found = pick;
+    if (pick >= 0) found = pick;
   }
   __syncthreads();
   if (tid == 0) {
-    const int pick = found >= 0 ? found : max(lo, hi - 1);
+    int pick = found;
+    if (pick < 0) {   // rounding left no bracket: the slice's last token still in play
+      pick = max(lo, hi - 1);
+      for (int e = hi - 1; e >= lo; --e)
+        if (!excl || !excluded(e)) {
+          pick = e;
+          break;
+        }
+    }
     out[s] = pick;
     if (out2) out2[(int64_t)s * out2_stride] = pick;
   }
@@ -479,12 +516,12 @@ size_t sample_workspace(int b) { return (size_t)b * kSampSlices * sizeof(SampPar
 
 hipError_t run_sample_rows(const float* base, int64_t seq_stride, const int* row_sel, int b, int V,
                            float temperature, uint64_t seed, uint64_t step, uint64_t draw, int* out,
-                           void* ws, hipStream_t st, int* out2, int out2_stride) {
+                           void* ws, hipStream_t st, int* out2, int out2_stride, const int* excl) {
   SampPart* parts = static_cast<SampPart*>(ws);
   hipLaunchKernelGGL(sample_part, dim3((unsigned)b * kSampSlices), dim3(kSampThreads), 0, st, base,
                      seq_stride, row_sel, V, temperature, parts);
   hipLaunchKernelGGL(sample_pick, dim3(b), dim3(kSampThreads), 0, st, base, seq_stride, row_sel, V,
-                     temperature, seed, step, draw, parts, out, out2, out2_stride);
+                     temperature, seed, step, draw, parts, excl, out, out2, out2_stride);
   return hipGetLastError();
 }
 

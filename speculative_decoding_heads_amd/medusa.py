@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmedusa.so")
 F32, BF16 = 0, 1
 GREEDY, TYPICAL = 0, 1
 ROOT_GIVEN = 2          # root_mode only: root[] is an input
+REJECT = 3              # acceptance mode only: exact rejection sampling
 MAX_K = 16              # shortlist size per head at most (columns of a rate table)
 MAX_T = 256
 

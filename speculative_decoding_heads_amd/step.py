@@ -38,7 +38,9 @@ class VerifyStep:
         self.device = device
         dt = M.BF16 if c.dtype == "bf16" else M.F32
         self.dt = dt
-        self.mode = M.TYPICAL if c.mode == "typical" else M.GREEDY
+        # acceptance mode; the root is drawn (typical, rejection) or the argmax
+        self.mode = {"greedy": M.GREEDY, "typical": M.TYPICAL, "reject": M.REJECT}[c.mode]
+        self.root_mode = M.GREEDY if self.mode == M.GREEDY else M.TYPICAL
         self.N = c.N
         T, K = c.T, c.K
         i32 = dict(dtype=torch.int32, device=device)
@@ -76,7 +78,7 @@ class VerifyStep:
         c = self.cfg
         M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
                        stream=stream)
-        root_mode = M.ROOT_GIVEN if root_given else self.mode
+        root_mode = M.ROOT_GIVEN if root_given else self.root_mode
         root = self.bonus if root_given else self.root
         if fused and self.plan is not None:
             M.medusa_topk_tree_tables(self.logits, c.k, c.kmax, self.plan[0], self.plan[1],
@@ -91,7 +93,7 @@ class VerifyStep:
         else:
             if self.plan is not None:
                 raise ValueError("a given tree plan needs the fused path")
-            M.medusa_topk(self.logits, c.k, c.kmax, self.mode, c.temperature, c.seed, step,
+            M.medusa_topk(self.logits, c.k, c.kmax, self.root_mode, c.temperature, c.seed, step,
                           self.root, self.idx, self.val, self.ws_topk, stream=stream)
             M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
                                 self.idx, x["seq_len"], self.tokens, self.pos, self.parent,

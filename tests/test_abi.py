@@ -112,9 +112,16 @@ def test_validation_before_launch():
                               None, 0, None) == ERR_ARG
     assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 300, 4, 4, 128, 400, 0.1, 1, fake,
                               None, 0, None) == ERR_ARG
-    # accept: bad mode, typical without temperature, small workspace
-    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 3, 1.0, 0.3, 0.09, 0, 0, fake, fake,
+    # accept: bad mode, typical / rejection without temperature, small workspace
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 4, 1.0, 0.3, 0.09, 0, 0, fake, fake,
                            fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, M.REJECT, 0.0, 0.3, 0.09, 0, 0, fake,
+                           fake, fake, fake, fake, 1 << 20, None) == ERR_ARG
+    assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, M.REJECT, 1.0, 0.3, 0.09, 0, 0, fake,
+                           fake, fake, fake, fake, 0, None) == ERR_WORKSPACE
+    assert M.medusa_verify_workspace(1 << 20, 128, 32000, M.BF16, M.REJECT) == \
+        M.medusa_verify_workspace(1 << 20, 128, 32000, M.BF16, M.TYPICAL)
+    assert M.medusa_verify_workspace(1 << 20, 128, 32000, M.BF16, 4) == 0
     assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 1, -1.0, 0.3, 0.09, 0, 0, fake, fake,
                            fake, fake, fake, 1 << 20, None) == ERR_ARG
     assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 0, 1.0, 0.3, 0.09, 0, 0, fake, fake,
