@@ -338,6 +338,8 @@ def main():
                     help="skip the measured copy / read / vendor-GEMM reference rates")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--mode", default="", choices=["", "greedy", "typical", "reject"],
+                    help="override the workloads' acceptance mode")
     ap.add_argument("--tree-sweep", default="",
                     help="comma-separated candidate counts: measure the tree budget "
                          "(expected tokens per second per tree size) on the workload")
@@ -355,6 +357,8 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
     cfg = C.BY_NAME[args.workload]
+    if args.mode:
+        cfg = cfg.with_(mode=args.mode)
     ms, per_call = measure(cfg, args.steps, args.warmup, args.rotate, log)
     value = 1000.0 / ms
     ab, af = alg_bytes(cfg), alg_flops(cfg)
@@ -390,6 +394,8 @@ def main():
     }
     if args.also:
         c2 = C.BY_NAME[args.also]
+        if args.mode:
+            c2 = c2.with_(mode=args.mode)
         ms2, pc2 = measure(c2, args.steps, args.warmup, None, log)
         b2 = sum(alg_bytes(c2).values())
         out["also"] = {"workload": c2.name, "value": round(1000.0 / ms2, 2),

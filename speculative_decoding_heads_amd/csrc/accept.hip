@@ -49,8 +49,10 @@ namespace medusa {
 constexpr int kStatThreads = 1024;
 
 // One 1024-thread workgroup per node row; each lane issues a group of 16-byte
-// loads before using any, then folds them into its argmax key (greedy) or its
-// online (m, s, t) state (typical); waves reduce by shuffles, LDS joins waves.
+// loads before using any, then folds them into its argmax key (greedy: a
+// float compare per value, one key per pass) or its (m, s, t) state (typical:
+// the pass's max, one exponential per value, one merge); waves reduce by
+// shuffles, LDS joins waves.
 template <int MODE>
 __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __restrict__ logits,
                                                              int V, float inv_temp,
@@ -80,13 +82,46 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __rest
         const int e = base + u * kStatThreads + tid;
         v[u] = e < nv ? *reinterpret_cast<const f32x4*>(x + 4 * e) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      if (MODE == kGreedy) {
+        // this pass's largest value at its lowest index (indices rise along
+        // the loop, so a strict '>' keeps the first of equal values; -0.0 and
+        // +0.0 compare equal, as in the key), then one key
+        float bv = -INFINITY;
+        int bi = -1;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = base + u * kStatThreads + tid;
-        if (e < nv) {
+        for (int u = 0; u < U; ++u) {
+          const int e = base + u * kStatThreads + tid;
+          if (e < nv) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) take(v[u][q], 4 * e + q);
+            for (int q = 0; q < 4; ++q) {
+              const bool tk = bi < 0 || v[u][q] > bv;
+              bv = tk ? v[u][q] : bv;
+              bi = tk ? 4 * e + q : bi;
+            }
+          }
         }
+        if (bi >= 0) take(bv, bi);
+      } else {
+        // this pass's values: their max first, then one exponential each, then
+        // a single merge into the running statistics (no per-value rescale)
+        float pm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (base + u * kStatThreads + tid < nv)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pm = fmaxf(pm, v[u][q] * inv_temp);
+        float ps = 0.f, pt = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (base + u * kStatThreads + tid < nv)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float d = v[u][q] * inv_temp - pm;
+              const float ex = __expf(d);
+              ps += ex;
+              pt = fmaf(ex, d, pt);
+            }
+        if (ps > 0.f) stat_merge(m, s, t, pm, ps, pt);
       }
     }
   } else {
@@ -231,7 +266,7 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
     // draw 16 d + j keyed by splitmix64(seed); the walk takes the first
     // accepted child at every node.
     __shared__ double sp[kMaxT];
-    __shared__ int first_acc[kMaxT];
+    __shared__ int first_acc[kMaxT], first_kid[kMaxT], sj[kMaxT];
     if (tid < T) {
       double pc = 0.0;
       if (my_valid) {
@@ -240,16 +275,23 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
       }
       sp[tid] = pc;
       first_acc[tid] = T;
+      first_kid[tid] = T;
     }
     __syncthreads();
+    if (tid > 0 && tid < T && my_parent >= 0 && my_parent < tid) atomicMin(&first_kid[my_parent], tid);
+    __syncthreads();
+    if (tid < T) sj[tid] = 0;
     if (tid < T && my_valid) {
+      // the earlier siblings: from the parent's first child (siblings follow
+      // one another in node order, so this is at most kmax - 1 steps)
       double r = 0.0;
       int j = 0;
-      for (int c = 1; c < tid; ++c)
+      for (int c = first_kid[my_parent]; c < tid; ++c)
         if (sparent[c] == my_parent) {
           r += sp[c];
           ++j;
         }
+      sj[tid] = j;
       const uint64_t draw = (uint64_t)(16 * sdepth[my_parent] + j);
       const double u = counter_uniform(splitmix64(seed), step, (uint64_t)s, draw);
       if (u * (1.0 - r) < sp[tid]) atomicMin(&first_acc[my_parent], tid);
@@ -267,18 +309,10 @@ __global__ __launch_bounds__(256) void accept_walk(const float* __restrict__ log
     __syncthreads();
     // the stop node's children were all rejected: the next token is drawn
     // without their tokens (none when it has no children)
-    if (tid < kSampExcl) {
-      int cnt = 0, tok = -1;
-      for (int c = 1; c < T; ++c)
-        if (sparent[c] == bestNode) {
-          if (cnt == tid) {
-            tok = stok[c];
-            break;
-          }
-          ++cnt;
-        }
-      excl[(int64_t)s * kSampExcl + tid] = tok;
-    }
+    if (tid < kSampExcl) excl[(int64_t)s * kSampExcl + tid] = -1;
+    __syncthreads();
+    if (my_valid && my_parent == bestNode && sj[tid] < kSampExcl)
+      excl[(int64_t)s * kSampExcl + sj[tid]] = stok[tid];
   } else {
     if (tid < T) {
       bool ok = tid == 0;
