@@ -46,6 +46,7 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkKPT = 32;          // entries kept per lane (rows up to 32768 entries)
 constexpr int kTopkCand = 2048;       // LDS candidate capacity
 constexpr int kTopkRankMax = 1024;    // rank selection for up to this many candidates
+static_assert(kTopkThreads >= kMaxT, "one thread per tree node");
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -62,16 +63,20 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
 
 // Tree tables of one sequence (fused with the shortlists, see topk_tree in
 // run_topk): position ids for every node and, from sequence 0, the static
-// parent / depth / ancestor tables.
-__device__ void tree_common(const TreeDev& t, const TreeOut& o, int s) {
+// parent / depth / ancestor tables.  Thread j handles node j (T <= the
+// workgroup size); the parents were staged in LDS (tpar) and node j's depth
+// in a register at the start of the kernel, so the ancestor walks read LDS.
+__device__ void tree_common(const TreeDev& t, const TreeOut& o, int s, const int16_t* tpar,
+                            int my_depth) {
   const int P = o.seq_len[s];
-  for (int j = threadIdx.x; j < t.T; j += blockDim.x) {
-    o.pos[(int64_t)s * t.T + j] = P + t.depth[j];
+  const int j = threadIdx.x;
+  if (j < t.T) {
+    o.pos[(int64_t)s * t.T + j] = P + my_depth;
     if (s == 0) {
-      o.parent[j] = t.parent[j];
-      o.depth[j] = t.depth[j];
+      o.parent[j] = tpar[j];
+      o.depth[j] = my_depth;
       uint64_t w[kMaxAncWords] = {0, 0, 0, 0};
-      for (int a = j; a >= 0; a = t.parent[a]) w[a >> 6] |= 1ull << (a & 63);
+      for (int a = j; a >= 0; a = tpar[a]) w[a >> 6] |= 1ull << (a & 63);
       for (int q = 0; q < t.anc_words; ++q)
         o.anc[(int64_t)j * t.anc_words + q] = q < kMaxAncWords ? w[q] : 0;
     }
@@ -100,9 +105,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
     }
   }
   const bool tree = to.tokens != nullptr;
+  // this row's tree tables, read before the logits so that they arrive while
+  // the row streams in: node tid's depth and rank, and the parents in LDS
+  __shared__ int16_t tpar[kMaxT];
+  int my_depth = -1, my_rank = 0;
+  if (tree && tid < t.T) {
+    tpar[tid] = t.parent[tid];
+    my_depth = t.depth[tid];
+    my_rank = t.rank[tid];
+  }
   if (k == 0) {            // root row: drawn by the sampler (typical) or given
     if (tree && i == 0) {
-      tree_common(t, to, s);
+      __syncthreads();     // tpar
+      tree_common(t, to, s, tpar, my_depth);
       if (a.root_mode == kRootGiven && tid == 0) to.tokens[(int64_t)s * t.T] = root[s];
     }
     return;
@@ -281,11 +296,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
   // ---- tree tokens: the nodes whose last rank lies in this head's shortlist
   __syncthreads();
   if (i == 0) {
-    tree_common(t, to, s);
+    tree_common(t, to, s, tpar, my_depth);
     if (tid == 0) to.tokens[(int64_t)s * t.T] = res[0];
-  } else {
-    for (int j = tid; j < t.T; j += kTopkThreads)
-      if (t.depth[j] == i) to.tokens[(int64_t)s * t.T + j] = res[t.rank[j]];
+  } else if (my_depth == i) {
+    to.tokens[(int64_t)s * t.T + tid] = res[my_rank];
   }
 }
 
