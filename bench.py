@@ -23,7 +23,7 @@ consecutive steps with the state carried on the device, captured in one HIP
 graph and replayed (reported under "loop"; `value` stays the single-step
 figure above).
 
-Prints ONE JSON line (rank 0).  --gpus N > 1 exits with a message: this build
+Prints ONE JSON line (rank 0).  --gpus N > 1 exits with a message: the step
 runs on one GPU.
 """
 
@@ -346,7 +346,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs the verify step on one GPU; --gpus {args.gpus} "
+        print(f"bench.py: the verify step runs on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported.", file=sys.stderr)
         sys.exit(2)
 

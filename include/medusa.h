@@ -60,7 +60,7 @@ typedef enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 } medusa_mode;
  * exact rejection sampling over the tree (see medusa_accept). */
 #define MEDUSA_REJECT 3
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MEDUSA_MAX_HEADS 16     /* Medusa heads K */
 #define MEDUSA_MAX_K 16         /* shortlist size per head */
 #define MEDUSA_MAX_T 256        /* tree nodes including the root */
