@@ -244,3 +244,36 @@ def test_tree_budget_argument_checks():
     assert L.medusa_topk_tree_tables(fake, 1, 2, 100, k, 2, good_p, good_r, 4, M.GREEDY, 1.0, 0, 0,
                                      fake, fake, fake, fake, fake, fake, fake, fake, fake, 0,
                                      fake, 1 << 20, None) == ERR_ARG            # anc_words < 1
+
+
+def test_empty_batch_is_a_noop_for_every_batched_call():
+    """b == 0 (rows == 0) returns MEDUSA_OK before any pointer is read or any
+    launch is made, for every entry point that takes a batch; the other
+    arguments are valid, the data pointers NULL."""
+    L = M.lib()
+    k = M._i32_host([4, 3])
+    par, _, rk = M.medusa_tree_plan((4, 3), 8)
+    ppar, prk = M._i32_host(list(par)), M._i32_host(list(rk))
+    T = len(par)
+    assert L.medusa_heads(None, 0, 256, None, 2, None, 100, M.BF16, 1, None, None, None, 0, None) == 0
+    assert L.medusa_verify_logits(None, 0, 256, None, 100, M.BF16, M.GREEDY, 1.0, None, None, 0,
+                                  None) == 0
+    assert L.medusa_topk(None, 0, 2, 100, k, 4, M.GREEDY, 1.0, 0, 0, None, None, None, None, 0,
+                         None) == 0
+    assert L.medusa_build_tree(k, 2, 8, 4, 5, None, None, 0, 4, None, None, None, None, None, None,
+                               1, None) == 0
+    assert L.medusa_topk_tree(None, 0, 2, 100, k, 4, 8, 4, 5, M.TYPICAL, 0.7, 0, 0, None, None,
+                              None, None, None, None, None, None, None, 1, None, 0, None) == 0
+    assert L.medusa_topk_tree_tables(None, 0, 2, 100, k, 4, ppar, prk, T, M.GREEDY, 1.0, 0, 0, None,
+                                     None, None, None, None, None, None, None, None, 1, None, 0,
+                                     None) == 0
+    assert L.medusa_tree_attn(None, None, None, None, None, 1, 0, T, 8, 2, 128, 100, 0.1, M.BF16,
+                              None, None, 0, None) == 0
+    for mode in (M.GREEDY, M.TYPICAL, M.REJECT):
+        assert L.medusa_accept(None, None, None, None, 0, T, 100, 2, mode, 0.7, 0.3, 0.09, 0, 0,
+                               None, None, None, None, None, 0, None) == 0
+        assert L.medusa_accept_compact(None, None, None, None, 0, T, 100, 2, mode, 0.7, 0.3, 0.09,
+                                       0, 0, None, None, None, None, None, None, None, 2, 100, 64,
+                                       M.BF16, None, None, 0, None) == 0
+    assert L.medusa_kv_compact(None, None, None, None, None, 0, 2, 100, 64, 2, M.BF16, None) == 0
+    assert L.medusa_accept_tally(None, None, 0, k, 2, ppar, prk, T, None, None, None) == 0
