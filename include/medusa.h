@@ -388,6 +388,47 @@ int medusa_accept_tally(const int32_t* L, const int32_t* path, int32_t b, const 
                         int32_t K, const int32_t* plan_parent, const int32_t* plan_rank,
                         int32_t T, int64_t* accepted, int64_t* offered, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * medusa_hydra_draft - Hydra-style sequentially dependent draft heads.
+ * zackli.ai "Speculative Decoding Deep Dive II: Medusa, MTP", "Medusa": the
+ * Medusa heads never see the token just drafted (accuracy falls with the
+ * offset); Hydra feeds that token to the later heads -- better drafts, less
+ * parallelism.  Reading taken (the pages give one sentence): head d of the
+ * residual form ([deep-dive] heads section) takes y = bf16(h + E[x]) in place
+ * of h, E [V,H] the base model's input embedding and x the token one position
+ * earlier on the candidate's path (the root for head 1):
+ *   u = bf16(y + SiLU(W_d y)),  logits = LM u  (f32),
+ * evaluated for every node of depth d-1; node (r_1..r_d) of the tree takes
+ * rank r_d of its parent's top-k_d (descending, ties to the lower index).
+ * With E = 0 this is the Medusa draft.  One LM pass per depth, sequential.
+ *
+ * h [b,H], E [V,H], W [K,H,H] (head d = W[d-1], out x in), LM [V,H]: bf16,
+ * device, 16-byte aligned; H % 128 == 0.  k_host[K], kmax, the tree as host
+ * tables plan_parent / plan_rank [T] (as for medusa_topk_tree_tables).  The
+ * root: argmax (MEDUSA_GREEDY) or seeded sample at `temperature`
+ * (MEDUSA_TYPICAL, counter draw 0) of LM h, or given in root[b]
+ * (MEDUSA_ROOT_GIVEN); tokens outside [0, V) read as the nearest end.
+ * Outputs (device) as medusa_topk_tree: root [b], tokens / pos [b,T] (pos =
+ * seq_len[s] + depth), parent / depth [T], anc [T][anc_words].  logits_out
+ * (optional, NULL = none) [b,T,V] f32: row (s, p) = the head logits that node
+ * p's children were drawn from, for every node above the deepest depth.
+ * ws: medusa_hydra_workspace() bytes, 16-byte aligned.  b * (the largest node
+ * count of a depth above the deepest) must not exceed 32767
+ * (MEDUSA_ERR_UNSUPPORTED).  The draft then feeds medusa_tree_attn and the
+ * rest of the step unchanged.
+ * ------------------------------------------------------------------------- */
+size_t medusa_hydra_workspace(int32_t b, int32_t H, int32_t V, const int32_t* k_host, int32_t K,
+                              int32_t kmax, const int32_t* plan_parent, const int32_t* plan_rank,
+                              int32_t T);
+int medusa_hydra_draft(const void* h, int32_t b, int32_t H, const void* E, int32_t V,
+                       const void* W, int32_t K, const void* LM, const int32_t* k_host,
+                       int32_t kmax, const int32_t* plan_parent, const int32_t* plan_rank,
+                       int32_t T, int32_t root_mode, float temperature, uint64_t seed,
+                       uint64_t step, const int32_t* seq_len, int32_t* root, int32_t* tokens,
+                       int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
+                       int32_t anc_words, float* logits_out, void* ws, size_t ws_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,8 @@ Sources (web pages on Medusa heads; cited by page title and section):
   * aicassindra.com "Medusa deep dive", "What it costs on a CPU-bound SLM":
     expected acceptance length as the throughput multiplier, the tree size as
     a tuned budget (module ``budget``).
+  * zackli.ai, "Speculative Decoding Deep Dive II" ("Medusa"): Hydra-style
+    heads that see the token just drafted (module ``hydra``).
 
 Every function states the passage it follows and, where the pages leave a step
 open, the reading taken.  Pins: ``tests/test_oracle_*.py``.
@@ -37,6 +39,7 @@ from .accept import (accept_greedy_walk, accept_greedy_parallel, accept_typical,
 from .compact import kv_compact
 from .step import oracle_step
 from .budget import tree_plan_rates, expected_tokens, plan_from_tables, accept_tally
+from .hydra import hydra_draft
 
 __all__ = [
     "round_bf16", "heads", "lm_project", "topk_stable", "argmax_lowest",
@@ -44,5 +47,5 @@ __all__ = [
     "full_tree_node_count", "full_path_count", "TreePlan", "tree_attention",
     "path_attention", "accept_greedy_walk", "accept_greedy_parallel",
     "accept_typical", "typical_local", "accept_reject", "kv_compact", "oracle_step",
-    "tree_plan_rates", "expected_tokens", "plan_from_tables", "accept_tally",
+    "tree_plan_rates", "expected_tokens", "plan_from_tables", "accept_tally", "hydra_draft",
 ]

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmedusa.so")
 
 SOURCES = ["api.cpp", "tree_plan.cpp", "gemm.hip", "topk.hip", "tree.hip", "attn.hip",
-           "accept.hip", "compact.hip", "loop.hip"]
+           "accept.hip", "compact.hip", "loop.hip", "hydra.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -330,6 +330,76 @@ static int topk_tree_common(const float* logits, int32_t b, int32_t K, int32_t V
   return hip_status(run_topk(logits, a, root, idx, val, ws, as_stream(stream), &t, &o), "topk_tree");
 }
 
+// ------------------------------------------------------------------- Hydra draft
+static std::shared_ptr<const TreePlanHost> hydra_plan(const int32_t* k_host, int32_t K,
+                                                      const int32_t* plan_parent,
+                                                      const int32_t* plan_rank, int32_t T,
+                                                      std::string* err) {
+  if (!k_host || K < 1 || K > MEDUSA_MAX_HEADS || !plan_parent || !plan_rank) {
+    *err = "need k_host, 1 <= K <= 16 and the plan tables";
+    return nullptr;
+  }
+  return plan_from_tables(k_host, K, plan_parent, plan_rank, T, err);
+}
+
+static TreeDev tree_dev(const TreePlanHost& p, int K, int kmax, int anc_words) {
+  TreeDev t{};
+  t.T = p.T; t.K = K; t.kmax = kmax; t.anc_words = anc_words;
+  for (int i = 0; i < p.T; ++i) {
+    t.parent[i] = (int16_t)p.parent[i];
+    t.depth[i] = (uint8_t)p.depth[i];
+    t.rank[i] = (uint8_t)(p.rank[i] < 0 ? 0 : p.rank[i]);
+  }
+  return t;
+}
+
+size_t medusa_hydra_workspace(int32_t b, int32_t H, int32_t V, const int32_t* k_host, int32_t K,
+                              int32_t kmax, const int32_t* plan_parent, const int32_t* plan_rank,
+                              int32_t T) {
+  if (b <= 0 || H <= 0 || V <= 0 || kmax < 1 || kmax > MEDUSA_MAX_K) return 0;
+  std::string err;
+  auto p = hydra_plan(k_host, K, plan_parent, plan_rank, T, &err);
+  if (!p) return 0;
+  return round_up(hydra_workspace(b, H, V, kmax, hydra_shape(tree_dev(*p, K, kmax, 1))));
+}
+
+int medusa_hydra_draft(const void* h, int32_t b, int32_t H, const void* E, int32_t V,
+                       const void* W, int32_t K, const void* LM, const int32_t* k_host,
+                       int32_t kmax, const int32_t* plan_parent, const int32_t* plan_rank,
+                       int32_t T, int32_t root_mode, float temperature, uint64_t seed,
+                       uint64_t step, const int32_t* seq_len, int32_t* root, int32_t* tokens,
+                       int32_t* pos, int32_t* parent, int32_t* depth, uint64_t* anc,
+                       int32_t anc_words, float* logits_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (int s = topk_tree_args(b, K, V, k_host, kmax, root_mode, temperature)) return s;
+  if (H <= 0) return fail(MEDUSA_ERR_ARG, "H must be positive");
+  if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "Hydra draft needs H % 128 == 0");
+  std::string err;
+  auto p = hydra_plan(k_host, K, plan_parent, plan_rank, T, &err);
+  if (!p) return fail(MEDUSA_ERR_ARG, err);
+  if (anc_words < (p->T + 63) / 64) return fail(MEDUSA_ERR_ARG, "anc_words < ceil(T / 64)");
+  if (b == 0) return MEDUSA_OK;
+  if (!h || !E || !W || !LM || !root || !seq_len || !tokens || !pos || !parent || !depth || !anc)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(h) || !aligned16(E) || !aligned16(W) || !aligned16(LM) || !aligned16(ws))
+    return fail(MEDUSA_ERR_ARG, "h, E, W, LM and the workspace must be 16-byte aligned");
+  const TreeDev t = tree_dev(*p, K, kmax, anc_words);
+  const HydraShape hs = hydra_shape(t);
+  int widest = 1;
+  for (int d = 0; d < hs.D; ++d) widest = hs.n[d] > widest ? hs.n[d] : widest;
+  if ((int64_t)b * widest > 32767) return fail(MEDUSA_ERR_UNSUPPORTED, "b * (widest depth) > 32767");
+  const size_t need = medusa_hydra_workspace(b, H, V, k_host, K, kmax, plan_parent, plan_rank, T);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "hydra: workspace too small");
+  TopkArgs a{};
+  a.b = b; a.K = K; a.V = V; a.kmax = kmax; a.root_mode = root_mode;
+  a.temperature = temperature; a.seed = seed; a.step = step;
+  for (int i = 0; i < K; ++i) a.k[i] = k_host[i];
+  TreeOut o{seq_len, tokens, pos, parent, depth, anc};
+  return hip_status(run_hydra_draft(h, E, W, LM, H, a, t, o, root, logits_out, ws,
+                                    as_stream(stream)),
+                    "hydra draft");
+}
+
 // ------------------------------------------------------------------- attention
 static int attn_check(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d, int32_t Pmax,
                       int32_t dtype) {

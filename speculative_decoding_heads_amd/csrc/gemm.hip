@@ -742,8 +742,8 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
 }
 
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st, bool rev) {
-  EpiLogits epi{logits, (int64_t)V, M, V};
+                         float* logits, hipStream_t st, bool rev, int64_t ldc) {
+  EpiLogits epi{logits, ldc > 0 ? ldc : (int64_t)V, M, V};
   if (dtype == kBF16)
     return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
                        H, epi, st, rev);

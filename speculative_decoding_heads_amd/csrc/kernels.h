@@ -21,8 +21,9 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
                             void* u, int R, int base, hipStream_t st);
 // rev: the weight-streaming kernel walks K backwards (same products, another
 // summation order); see medusa_heads.
+// ldc: logits row stride in floats (0: V).
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st, bool rev = false);
+                         float* logits, hipStream_t st, bool rev = false, int64_t ldc = 0);
 // LM projection of the verify rows plus acceptance partials per (row, weight
 // tile) in ws: header (kPartsHeader bytes: ntiles, typical, rows), then
 // [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).
@@ -64,6 +65,24 @@ size_t topk_workspace(int b, int K, int V, int kmax);
 hipError_t run_topk(const float* logits, const TopkArgs& a, int* root, int* idx, float* val,
                     void* ws, hipStream_t st, const TreeDev* tree = nullptr,
                     const TreeOut* tree_out = nullptr);
+
+// ---- Hydra-style sequential draft (hydra.hip)
+// Row counts of the plan's depths: n[d] nodes at depth d, first node first[d]
+// (nodes come in depth order).  Returns the largest parent row count
+// b * max_{d < D} n[d] the per-depth passes use (D = the deepest depth).
+struct HydraShape {
+  int D;
+  int first[kMaxHeads + 1], n[kMaxHeads + 1];
+};
+HydraShape hydra_shape(const TreeDev& t);
+size_t hydra_workspace(int b, int H, int V, int kmax, const HydraShape& hs);
+// h [b,H], E [V,H], W [K,H,H], LM [V,H] bf16; k per head in a.k; the root
+// as in run_topk (a.root_mode); the tree tables, positions and tokens into o;
+// logits_out (optional) [b,T,V]: row (s, p) = the head logits node p's
+// children were drawn from, for every node above the deepest depth.
+hipError_t run_hydra_draft(const void* h, const void* E, const void* W, const void* LM, int H,
+                           const TopkArgs& a, const TreeDev& t, const TreeOut& o, int* root,
+                           float* logits_out, void* ws, hipStream_t st);
 
 // ---- sampling rows of softmax(x / T) in float64 (topk.hip)
 // Row of sequence s: base + s*seq_stride + (row_sel ? row_sel[s] : 0) * V.

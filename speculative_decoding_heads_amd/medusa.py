@@ -71,6 +71,10 @@ _SIGS = {
     "medusa_topk_tree_tables": ([_P, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _F, _U64, _U64,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P], _I32),
     "medusa_accept_tally": ([_P, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P], _I32),
+    "medusa_hydra_workspace": ([_I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32], _SZ),
+    "medusa_hydra_draft": ([_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32,
+                            _F, _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P],
+                           _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -467,3 +471,38 @@ def medusa_next_hidden(O, path, L, h, stream=None):
     st = lib().medusa_next_hidden(_ptr(O), _ptr(path), _ptr(L), b, T, K, H, dtype_code(O), _ptr(h),
                                   _stream(stream))
     _check("medusa_next_hidden", st)
+
+
+def medusa_hydra_workspace(b, H, V, k, kmax, plan_parent, plan_rank):
+    return lib().medusa_hydra_workspace(b, H, V, _i32_host(k), len(k), kmax,
+                                        _i32_host(plan_parent), _i32_host(plan_rank),
+                                        len(plan_parent))
+
+
+def medusa_hydra_draft(h, E, W, LM, k, kmax, plan_parent, plan_rank, root_mode, temperature, seed,
+                       step, seq_len, root, tokens, pos, parent, depth, anc, ws, logits_out=None,
+                       stream=None):
+    """Hydra-style draft: per-depth heads on h + E[previous token] (bf16)."""
+    b, H = h.shape
+    V = E.shape[0]
+    K = len(k)
+    T = len(plan_parent)
+    _need(len(plan_rank) == T, "plan_rank: expected one rank per node")
+    _shape(E, (V, H), "E")
+    _shape(W, (K, H, H), "W")
+    _shape(LM, (V, H), "LM")
+    for t, n in ((h, "h"), (E, "E"), (W, "W"), (LM, "LM")):
+        _dt(t, torch.bfloat16, n)
+    _shape(root, (b,), "root")
+    _dt(root, torch.int32, "root")
+    _tree_shapes(T, b, seq_len, tokens, pos, parent, depth, anc)
+    if logits_out is not None:
+        _shape(logits_out, (b, T, V), "logits_out")
+        _dt(logits_out, torch.float32, "logits_out")
+    st = lib().medusa_hydra_draft(_ptr(h), b, H, _ptr(E), V, _ptr(W), K, _ptr(LM), _i32_host(k),
+                                  kmax, _i32_host(plan_parent), _i32_host(plan_rank), T, root_mode,
+                                  temperature, seed, step, _ptr(seq_len), _ptr(root), _ptr(tokens),
+                                  _ptr(pos), _ptr(parent), _ptr(depth), _ptr(anc), anc.shape[1],
+                                  _ptr(logits_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream))
+    _check("medusa_hydra_draft", st)

@@ -1,0 +1,151 @@
+"""Hydra-style draft (medusa_hydra_draft) on the GPU against the oracle.
+
+Stage-wise, as everywhere in this suite: the oracle computes every head's
+logits from the GPU's own parent tokens (oracle.hydra_draft with
+parent_tokens), so a near-tie at one depth cannot change what the next depth
+is compared against.  Checked per sequence:
+  * tree tables, ancestor words and position ids bit-exact;
+  * the root: given, or argmax / counter sample of LM h compared with the
+    oracle's when its decision is not within float32 rounding;
+  * every drawn-from row of logits_out within 2e-2 row-relative of the oracle;
+  * every child token bit-exact: rank r of the stable top-k of the GPU's own
+    row for its parent;
+  * a full step on a Hydra draft runs the rest of the pipeline unchanged.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (argmax_lowest, counter_uniform, hydra_draft, lm_project, plan_from_tables,
+                    sample_tempered, topk_stable, tree_plan)
+from speculative_decoding_heads_amd import medusa as M
+from tests.helpers import TOL_BF16, assert_rows_close, normal, np64, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+I32 = dict(dtype=torch.int32, device=DEV)
+TEMP = float(np.float32(0.7))
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _inputs(b, H, V, K, seed):
+    h = normal((b, H), seed, 1.0)
+    E = normal((V, H), seed + 1, 0.5)
+    W = normal((K, H, H), seed + 2, 0.05)
+    LM = normal((V, H), seed + 3, 0.05)
+    return h, E, W, LM
+
+
+def _run(h, E, W, LM, k, par, rk, mode, root_in, P, logits=True):
+    b, H = h.shape
+    V = E.shape[0]
+    T = len(par)
+    Wd = (T + 63) // 64
+    root = root_in.clone() if root_in is not None else torch.empty(b, **I32)
+    tokens, pos = torch.empty(b, T, **I32), torch.empty(b, T, **I32)
+    parent, depth = torch.empty(T, **I32), torch.empty(T, **I32)
+    anc = torch.empty(T, Wd, dtype=torch.int64, device=DEV)
+    lo = torch.zeros(b, T, V, dtype=torch.float32, device=DEV) if logits else None
+    ws = M.workspace(M.medusa_hydra_workspace(b, H, V, k, max(k), par, rk))
+    M.medusa_hydra_draft(h.to(DEV), E.to(DEV), W.to(DEV), LM.to(DEV), k, max(k), par, rk, mode, TEMP,
+                         0x5EED, 4, P, root, tokens, pos, parent, depth, anc, ws, logits_out=lo)
+    torch.cuda.synchronize()
+    return root, tokens, pos, parent, depth, anc, lo
+
+
+CASES = [((3, 2, 2), None, 3, 256, 3001), ((10,) * 4, 64, 2, 384, 4096), ((4, 3, 2, 2), 20, 4, 128, 999)]
+
+
+@pytest.mark.parametrize("k,N,b,H,V", CASES)
+@pytest.mark.parametrize("mode", ["given", "greedy", "typical"])
+def test_hydra_draft_matches_oracle(k, N, b, H, V, mode):
+    say("hydra", k, N, b, H, V, mode)
+    K = len(k)
+    par, _, rk = M.medusa_tree_plan(k, N)
+    plan = plan_from_tables(k, par, rk)
+    T = plan.T
+    h, E, W, LM = _inputs(b, H, V, K, 100 + V)
+    rng = np.random.default_rng(V)
+    given = torch.from_numpy(rng.integers(0, V, size=b).astype(np.int32)).to(DEV)
+    P = torch.from_numpy(rng.integers(0, 5000, size=b).astype(np.int32)).to(DEV)
+    m = {"given": M.ROOT_GIVEN, "greedy": M.GREEDY, "typical": M.TYPICAL}[mode]
+    root, tokens, pos, parent, depth, anc, lo = _run(h, E, W, LM, k, par, rk, m,
+                                                     given if mode == "given" else None, P)
+    assert list(parent.cpu().numpy()) == list(plan.parent)
+    assert list(depth.cpu().numpy()) == list(plan.depth)
+    a = anc.cpu().numpy().view(np.uint64)
+    for i in range(T):
+        for j in range(T):
+            assert bool((int(a[i, j // 64]) >> (j % 64)) & 1) == bool(plan.anc[i, j])
+    hf, Ef, Wf, LMf = np64(h), np64(E), np64(W), np64(LM)
+    tok, lgo, r_gpu = tokens.cpu().numpy(), lo.cpu().numpy(), root.cpu().numpy()
+    Pn = P.cpu().numpy()
+    checked_root = 0
+    for s in range(b):
+        assert list(pos[s].cpu().numpy()) == list(Pn[s] + plan.depth)
+        assert tok[s, 0] == r_gpu[s]
+        row0 = lm_project(hf[s][None, :], LMf)[0]
+        if mode == "given":
+            assert r_gpu[s] == int(given[s])
+        elif mode == "greedy":
+            srt = np.sort(row0)
+            if srt[-1] - srt[-2] > 1e-4 * np.abs(row0).max():
+                assert r_gpu[s] == argmax_lowest(row0)
+                checked_root += 1
+        else:
+            u = counter_uniform(0x5EED, 4, s, 0)
+            want, c = sample_tempered(row0, TEMP, u)
+            if np.min(np.abs(c - u * c[-1])) / c[-1] > 1e-4:
+                assert r_gpu[s] == want
+                checked_root += 1
+        _, rows = hydra_draft(hf[s], Ef, Wf, LMf, k, plan, int(r_gpu[s]), bf16=True,
+                              parent_tokens=tok[s])
+        for p, ref in rows.items():
+            assert_rows_close(lgo[s, p], ref, TOL_BF16, f"logits of node {p}")
+        for c in range(1, T):
+            p = int(plan.parent[c])
+            short = topk_stable(lgo[s, p], k[int(plan.depth[c]) - 1])
+            assert tok[s, c] == short[plan.tuples[c][-1]], (s, c)
+    if mode != "given":
+        assert checked_root >= 1
+
+
+def test_hydra_rates_tree_and_deep_chain():
+    """A rates-planned tree of depth 5 with uneven depth widths (the tables
+    path), no logits_out, b = 1."""
+    k = (6, 3, 2, 2, 2)
+    q = np.zeros((5, 16))
+    for d, s in enumerate(k):
+        q[d, :s] = 0.9 / np.arange(1, s + 1)
+    par, _, rk, _ = M.medusa_tree_plan_rates(k, 30, q)
+    plan = plan_from_tables(k, par, rk)
+    assert max(plan.depth) == 5
+    h, E, W, LM = _inputs(1, 256, 2000, 5, 7)
+    P = torch.tensor([123], **I32)
+    root, tokens, *_ = _run(h, E, W, LM, k, par, rk, M.GREEDY, None, P, logits=False)
+    _, tokens2, *_, lo = _run(h, E, W, LM, k, par, rk, M.ROOT_GIVEN, root, P)
+    assert torch.equal(tokens, tokens2)        # logits_out changes nothing
+    tok = tokens.cpu().numpy()[0]
+    lgo = lo.cpu().numpy()[0]
+    _, rows = hydra_draft(np64(h)[0], np64(E), np64(W), np64(LM), k, plan, int(tok[0]),
+                          parent_tokens=tok)
+    for p, ref in rows.items():
+        assert_rows_close(lgo[p], ref, TOL_BF16, f"logits of node {p}")
+    for c in range(1, plan.T):
+        p = int(plan.parent[c])
+        assert tok[c] == topk_stable(lgo[p], k[int(plan.depth[c]) - 1])[plan.tuples[c][-1]]
+
+
+def test_hydra_single_node_tree_is_root_only():
+    par, _, rk = M.medusa_tree_plan((4,), 0)
+    assert len(par) == 1
+    h, E, W, LM = _inputs(2, 128, 500, 1, 9)
+    P = torch.tensor([5, 9], **I32)
+    root, tokens, pos, *_ = _run(h, E, W, LM, (4,), par, rk, M.GREEDY, None, P, logits=False)
+    assert torch.equal(tokens[:, 0], root)
+    assert pos.cpu().numpy().tolist() == [[5], [9]]
