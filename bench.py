@@ -75,8 +75,18 @@ def _enqueue(st, x, step, M, c, ev=None):
         if ev is not None:
             ev[i].record()
     mark(0)
-    M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
-    mark(1)
+    if st.draft == "hydra":            # the whole draft counts as draft_heads
+        st.draft_hydra(x, step, st.root_mode, st.root)
+        mark(1)
+    else:
+        M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
+        mark(1)
+        _shortlists(st, x, step, M, c)
+    mark(2)
+    _verify(st, x, step, M, c, mark)
+
+
+def _shortlists(st, x, step, M, c):
     if st.plan is not None:
         M.medusa_topk_tree_tables(st.logits, c.k, c.kmax, st.plan[0], st.plan[1], st.root_mode,
                                   c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
@@ -86,7 +96,9 @@ def _enqueue(st, x, step, M, c, ev=None):
         M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
                            st.root_mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
                            st.val, st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
-    mark(2)
+
+
+def _verify(st, x, step, M, c, mark):
     M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
     mark(3)
     M.medusa_verify_logits(st.O.view(c.b * c.T, c.nq * c.d), x["LM"],
@@ -100,7 +112,7 @@ def _enqueue(st, x, step, M, c, ev=None):
     mark(5)
 
 
-def measure(cfg, steps, warmup, rotate=None, log=print, plan=None):
+def measure(cfg, steps, warmup, rotate=None, log=print, plan=None, draft="medusa"):
     import torch
     from speculative_decoding_heads_amd import medusa as M
     from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
@@ -109,7 +121,8 @@ def measure(cfg, steps, warmup, rotate=None, log=print, plan=None):
     M.lib()
     c = cfg
     t0 = time.time()
-    host = make_inputs(c)
+    names = ("h", "W", "LM", "Kc", "Vc", "Q") + (("E",) if draft == "hydra" else ())
+    host = make_inputs(c, names)
     ws_bytes = sum(v.numel() * v.element_size() for v in host.values())
     if rotate is None:
         rotate = 2 if ws_bytes < (1 << 30) else 1
@@ -120,7 +133,7 @@ def measure(cfg, steps, warmup, rotate=None, log=print, plan=None):
     del host
     log(f"[bench] {c.name}: inputs {ws_bytes / 1e6:.1f} MB x {rotate} copies "
         f"({time.time() - t0:.1f}s)")
-    st = VerifyStep(c, plan=plan)
+    st = VerifyStep(c, plan=plan, draft=draft)
     n = warmup + 2 * steps
     seqs = [torch.full((c.b,), c.P, dtype=torch.int32, device="cuda") for _ in range(n)]
 
@@ -340,6 +353,9 @@ def main():
                     help="run one device copy of this many MiB first (counter calibration)")
     ap.add_argument("--mode", default="", choices=["", "greedy", "typical", "reject"],
                     help="override the workloads' acceptance mode")
+    ap.add_argument("--hydra", action="store_true",
+                    help="also time the step with the Hydra-style draft (medusa_hydra_draft: "
+                         "one LM pass per tree depth) on the same workload")
     ap.add_argument("--tree-sweep", default="",
                     help="comma-separated candidate counts: measure the tree budget "
                          "(expected tokens per second per tree size) on the workload")
@@ -402,6 +418,11 @@ def main():
                        "unit": "verify-steps/s", "ms_per_step": round(ms2, 4),
                        "step_effective_GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
                        "per_call_us": {k: round(v, 2) for k, v in pc2.items()}}
+    if args.hydra:
+        ms_h, pch = measure(cfg, args.steps, args.warmup, args.rotate, log, draft="hydra")
+        out["hydra"] = {"workload": cfg.name, "draft": "hydra", "value": round(1000.0 / ms_h, 2),
+                        "unit": "verify-steps/s", "ms_per_step": round(ms_h, 4),
+                        "per_call_us": {k: round(v, 2) for k, v in pch.items()}}
     if args.loop > 0:
         ms_l = measure_loop(cfg, args.loop, args.loop_replays, log=log)
         out["loop"] = {"workload": cfg.name, "value": round(1000.0 / ms_l, 2),

@@ -24,11 +24,18 @@ from . import medusa as M
 
 
 class VerifyStep:
-    def __init__(self, cfg, device="cuda", plan=None):
+    def __init__(self, cfg, device="cuda", plan=None, draft="medusa"):
         """plan: optional host tables (parent, rank) of the tree, e.g. from
         medusa_tree_plan_rates (the tree budget); default: the fixed tree of
-        cfg.N candidates.  Either way the tree has cfg.T nodes."""
+        cfg.N candidates.  Either way the tree has cfg.T nodes.
+
+        draft: "medusa" (the K heads on h, one launch for shortlists + tree) or
+        "hydra" (medusa_hydra_draft: head d on h + E[previous token], one LM
+        pass per depth; bf16 and the fused path only; x needs "E")."""
         self.cfg = c = cfg
+        if draft not in ("medusa", "hydra"):
+            raise ValueError("draft must be 'medusa' or 'hydra'")
+        self.draft = draft
         if plan is not None:
             parent, rank = list(plan[0]), list(plan[1])
             if len(parent) != c.T or len(rank) != c.T:
@@ -69,17 +76,35 @@ class VerifyStep:
         self.ws_acc = M.workspace(M.medusa_accept_workspace(c.b, T), device)
         self.ws_verify = M.workspace(
             M.medusa_verify_workspace(c.b * T, c.nq * c.d, c.V, dt, self.mode), device)
+        if draft == "hydra":
+            if dt != M.BF16:
+                raise ValueError("the Hydra draft runs in bf16")
+            if self.plan is None:
+                par, _, rk = M.medusa_tree_plan(c.k, c.N, c.decay.numerator, c.decay.denominator)
+                self.plan = (list(par), list(rk))
+            self.ws_hydra = M.workspace(
+                M.medusa_hydra_workspace(c.b, c.H, c.V, c.k, c.kmax, *self.plan), device)
 
     def run(self, x, step=0, stream=None, fused=True, root_given=False):
         """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len.
 
         root_given: the tree root is the previous step's next token (self.bonus)
         instead of the base head's argmax / sample (fused path only)."""
+        root_mode = M.ROOT_GIVEN if root_given else self.root_mode
+        root = self.bonus if root_given else self.root
+        if self.draft == "hydra":
+            if not fused:
+                raise ValueError("the Hydra draft needs the fused path")
+            self.draft_hydra(x, step, root_mode, root, stream)
+        else:
+            self.draft_medusa(x, step, root_mode, root, fused, stream)
+        self.verify(x, step, fused, stream)
+
+    def draft_medusa(self, x, step, root_mode, root, fused, stream=None):
+        """The Medusa draft of one step: head logits, root, shortlists and tree."""
         c = self.cfg
         M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
                        stream=stream)
-        root_mode = M.ROOT_GIVEN if root_given else self.root_mode
-        root = self.bonus if root_given else self.root
         if fused and self.plan is not None:
             M.medusa_topk_tree_tables(self.logits, c.k, c.kmax, self.plan[0], self.plan[1],
                                       root_mode, c.temperature, c.seed, step, x["seq_len"], root,
@@ -98,6 +123,18 @@ class VerifyStep:
             M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
                                 self.idx, x["seq_len"], self.tokens, self.pos, self.parent,
                                 self.depth, self.anc, stream=stream)
+
+    def draft_hydra(self, x, step, root_mode, root, stream=None):
+        """The Hydra-style draft of one step: root, tree tables and tokens."""
+        c = self.cfg
+        M.medusa_hydra_draft(x["h"], x["E"], x["W"], x["LM"], c.k, c.kmax, self.plan[0],
+                             self.plan[1], root_mode, c.temperature, c.seed, step, x["seq_len"],
+                             root, self.tokens, self.pos, self.parent, self.depth, self.anc,
+                             self.ws_hydra, stream=stream)
+
+    def verify(self, x, step, fused, stream=None):
+        """Tree attention, verification logits, acceptance and KV rollback."""
+        c = self.cfg
         M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], self.anc, self.O,
                            ws=self.ws_attn, stream=stream)
         if fused:
@@ -155,6 +192,7 @@ class VerifyLoop:
         with torch.cuda.graph(g):
             self.run(x, Qs, Kn, Vn, step0=step0, root_given_first=root_given_first)
         return g
+
 
 
 def loop_inputs(cfg, steps, seed_base=0, device="cuda"):

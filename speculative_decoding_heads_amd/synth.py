@@ -16,7 +16,7 @@ stays bounded.
 
 import torch
 
-TENSOR_IDS = {"h": 0, "W": 1, "LM": 2, "Kc": 3, "Vc": 4, "Q": 5}
+TENSOR_IDS = {"h": 0, "W": 1, "LM": 2, "Kc": 3, "Vc": 4, "Q": 5, "E": 6}
 WEIGHT_STD = 0.02
 
 
@@ -55,7 +55,8 @@ def make_inputs(cfg, names=("h", "W", "LM", "Kc", "Vc", "Q")):
 
     h [b, H]; W [K, H, H] ([head, out, in]); LM [V, H];
     Kc, Vc [b, nkv, Pmax, d] with the tree nodes' K/V at slots P..P+T-1;
-    Q [b, T, nq, d] (the tree nodes' queries).
+    Q [b, T, nq, d] (the tree nodes' queries); on request E [V, H], the input
+    embedding table a Hydra-style draft adds to h (N(0, 1), the scale of h).
     """
     shapes = {
         "h": (cfg.b, cfg.H),
@@ -64,6 +65,7 @@ def make_inputs(cfg, names=("h", "W", "LM", "Kc", "Vc", "Q")):
         "Kc": (cfg.b, cfg.nkv, cfg.Pmax, cfg.d),
         "Vc": (cfg.b, cfg.nkv, cfg.Pmax, cfg.d),
         "Q": (cfg.b, cfg.T, cfg.nq, cfg.d),
+        "E": (cfg.V, cfg.H),
     }
     out = {}
     for n in names:

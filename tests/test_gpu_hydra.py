@@ -149,3 +149,29 @@ def test_hydra_single_node_tree_is_root_only():
     root, tokens, pos, *_ = _run(h, E, W, LM, (4,), par, rk, M.GREEDY, None, P, logits=False)
     assert torch.equal(tokens[:, 0], root)
     assert pos.cpu().numpy().tolist() == [[5], [9]]
+
+
+def test_step_on_a_hydra_draft():
+    """VerifyStep(draft="hydra"): the draft equals a direct medusa_hydra_draft
+    call, and the rest of the step (attention, verification, acceptance,
+    rollback) runs on it: the accepted path follows the tree and seq_len
+    advances by L + 1."""
+    from speculative_decoding_heads_amd import configs as C
+    from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
+    from speculative_decoding_heads_amd.synth import make_inputs
+    cfg = C.Config("hydra_step", 97, 2, 256, 3000, (4, 3, 2), 20, 4, 2, 64, 200, "bf16", "greedy")
+    host = make_inputs(cfg, ("h", "W", "LM", "Kc", "Vc", "Q", "E"))
+    x = device_inputs(cfg, host)
+    st = VerifyStep(cfg, draft="hydra")
+    st.run(x, step=1)
+    torch.cuda.synchronize()
+    par, rk = st.plan
+    root, tokens, *_ = _run(host["h"], host["E"], host["W"], host["LM"], cfg.k, par, rk, M.GREEDY,
+                            None, torch.full((cfg.b,), cfg.P, **I32), logits=False)
+    assert torch.equal(st.tokens, tokens) and torch.equal(st.root, root)
+    L, path = st.L.cpu().numpy(), st.path.cpu().numpy()
+    for s in range(cfg.b):
+        assert 0 <= L[s] <= cfg.K and path[s, 0] == 0
+        for d in range(1, L[s] + 1):
+            assert par[path[s, d]] == path[s, d - 1]
+    assert torch.equal(x["seq_len"].cpu(), torch.from_numpy(cfg.P + L + 1).int())
