@@ -277,3 +277,31 @@ def test_empty_batch_is_a_noop_for_every_batched_call():
                                        M.BF16, None, None, 0, None) == 0
     assert L.medusa_kv_compact(None, None, None, None, None, 0, 2, 100, 64, 2, M.BF16, None) == 0
     assert L.medusa_accept_tally(None, None, 0, k, 2, ppar, prk, T, None, None, None) == 0
+
+
+def test_hydra_draft_argument_checks():
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)
+    k = M._i32_host([4, 3])
+    par, _, rk = M.medusa_tree_plan((4, 3), 8)
+    pp, pr = M._i32_host(list(par)), M._i32_host(list(rk))
+    T = len(par)
+
+    def call(b=1, H=256, kk=k, K=2, kmax=4, ppar=pp, prk=pr, T_=T, mode=M.GREEDY, temp=1.0,
+             aw=1, ws_bytes=1 << 30, h=fake):
+        return L.medusa_hydra_draft(h, b, H, fake, 100, fake, K, fake, kk, kmax, ppar, prk, T_,
+                                    mode, temp, 0, 0, fake, fake, fake, fake, fake, fake, fake, aw,
+                                    None, fake, ws_bytes, None)
+    assert call(H=200) == ERR_UNSUPPORTED                    # H % 128
+    assert call(mode=M.TYPICAL, temp=0.0) == ERR_ARG         # typical root needs a temperature
+    assert call(mode=5) == ERR_ARG
+    bad_parent = M._i32_host([-1, 0, 3] + list(par[3:]))
+    assert call(ppar=bad_parent) == ERR_ARG                  # parent after its child
+    assert call(T_=T, prk=M._i32_host([-1] + [9] * (T - 1))) == ERR_ARG   # rank >= k
+    assert call(aw=0) == ERR_ARG                             # anc words
+    assert call(ws_bytes=16) == ERR_WORKSPACE
+    assert call(h=ctypes.c_void_p(0x1008)) == ERR_ARG        # alignment
+    assert call(b=0, h=None) == 0                            # empty batch
+    need = M.medusa_hydra_workspace(1, 256, 100, [4, 3], 4, list(par), list(rk))
+    assert need > 0 and need % 256 == 0
+    assert M.medusa_hydra_workspace(2, 256, 100, [4, 3], 4, list(par), list(rk)) > need
