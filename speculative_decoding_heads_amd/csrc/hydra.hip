@@ -151,7 +151,10 @@ hipError_t run_hydra_draft(const void* h, const void* E, const void* W, const vo
     if (e != hipSuccess) return e;
     e = run_heads_hidden(y, rows, H, Wb + (size_t)(d - 1) * H * H, 1, kBF16, u, 1, 0, st);
     if (e != hipSuccess) return e;
-    e = run_lm_logits(u, rows, H, LM, V, kBF16, lg + V, st, false, 2 * (int64_t)V);
+    // consecutive passes walk the weights' K chunks in opposite directions, so
+    // each starts on what the previous pass read last (still in the last-level
+    // cache); the root pass, when there is one, walks forwards
+    e = run_lm_logits(u, rows, H, LM, V, kBF16, lg + V, st, (d & 1) != 0, 2 * (int64_t)V);
     if (e != hipSuccess) return e;
     if (logits_out) {
       hipLaunchKernelGGL(hydra_copy_rows, dim3(rows), dim3(256), 0, st, lg, V, t.T, first, n,
