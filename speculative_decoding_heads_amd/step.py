@@ -168,12 +168,13 @@ class VerifyLoop:
     Every call only enqueues kernels, so ``run`` can be captured in a HIP
     graph (``capture``) and replayed."""
 
-    def __init__(self, cfg, device="cuda", plan=None):
+    def __init__(self, cfg, device="cuda", plan=None, draft="medusa"):
         self.cfg = cfg
-        self.step = VerifyStep(cfg, device, plan)
+        self.step = VerifyStep(cfg, device, plan, draft)
 
     def run(self, x, Qs, Kn, Vn, step0=0, root_given_first=False, stream=None, after_step=None):
-        """x: h, W, LM, Kc, Vc, seq_len (state, updated in place); Qs [S, b, T, nq, d],
+        """x: h, W, LM (and E for the Hydra draft), Kc, Vc, seq_len (state, updated
+        in place); Qs [S, b, T, nq, d],
         Kn / Vn [S, b, nkv, T, d].  after_step(s) runs after each step (eager use only)."""
         st = self.step
         for s in range(Qs.shape[0]):

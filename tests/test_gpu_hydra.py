@@ -175,3 +175,38 @@ def test_step_on_a_hydra_draft():
         for d in range(1, L[s] + 1):
             assert par[path[s, d]] == path[s, d - 1]
     assert torch.equal(x["seq_len"].cpu(), torch.from_numpy(cfg.P + L + 1).int())
+
+
+def test_hydra_loop_graph_replay_equals_eager():
+    """Three loop steps on the Hydra draft (steps 1 and 2 take the previous
+    next token as the root, so the draft skips its root pass): a HIP graph of
+    the loop, replayed once, leaves the same state bit for bit as the eager
+    run."""
+    from speculative_decoding_heads_amd import configs as C
+    from speculative_decoding_heads_amd.step import VerifyLoop, device_inputs, loop_inputs
+    from speculative_decoding_heads_amd.synth import make_inputs
+    cfg = C.Config("hydra_loop", 96, 2, 256, 3000, (4, 3, 2), 20, 4, 2, 64, 150, "bf16", "typical")
+    steps = 3
+    host = make_inputs(cfg, ("h", "W", "LM", "Kc", "Vc", "Q", "E"))
+    Qs, Kn, Vn = loop_inputs(cfg, steps, seed_base=55)
+    cap = cfg.P + steps * (cfg.K + 1) + cfg.T
+    states = []
+    for use_graph in (False, True):
+        x = device_inputs(cfg, host)
+        for name in ("Kc", "Vc"):
+            big = torch.zeros(cfg.b, cfg.nkv, cap, cfg.d, dtype=x[name].dtype, device=DEV)
+            big[:, :, : cfg.P] = x[name][:, :, : cfg.P]
+            x[name] = big
+        loop = VerifyLoop(cfg, draft="hydra")
+        if use_graph:
+            g = loop.capture(x, Qs, Kn, Vn)
+            g.replay()
+        else:
+            loop.run(x, Qs, Kn, Vn)
+        torch.cuda.synchronize()
+        st = loop.step
+        states.append([t.clone() for t in (x["h"], x["Kc"], x["Vc"], x["seq_len"], st.tokens,
+                                           st.L, st.path, st.bonus)])
+    for a, c in zip(*states):
+        assert torch.equal(a, c)
+    assert int(states[0][3].min()) > cfg.P + steps - 1      # every step advanced seq_len
