@@ -17,11 +17,13 @@
 // and everything after the draft are the Medusa step's.
 //
 // Per depth d (sequential; one pass of the LM weights per depth):
-//   hydra_embed    y rows (s, parent j) = bf16(h[s] + e[token(parent)])
-//   gemm (heads)   u = y + SiLU(W_d y), bf16            (run_heads_hidden)
-//   gemm (LM)      logits of every parent row           (run_lm_logits)
-//   topk_rows      the parent rows' top-k_d             (run_topk, no root)
-//   hydra_children token(child) = shortlist(parent)[rank(child)]
+//   gemm (heads)   u = y + SiLU(W_d y), bf16, y the rows (s, node of depth d-1)
+//                  of bf16(h[s] + e[token])                 (run_heads_hidden)
+//   gemm (LM)      logits of every parent row               (run_lm_logits)
+//   topk_rows      the parent rows' top-k_d                 (run_topk, no root)
+//   hydra_next     token(child) = shortlist(parent)[rank(child)], and the
+//                  children's rows of y for depth d+1
+// (hydra_embed writes depth 1's rows from the root.)
 // The root (argmax / sample of LM h, or given) and the tree tables come from
 // one run_topk launch on the plan before depth 1.
 
@@ -30,18 +32,15 @@
 
 namespace medusa {
 
-// One workgroup per parent row r = s * n + j (node first + j): 16-byte pieces
-// of h[s] and e[tok] added in float, rounded to bf16 once.  Tokens outside
+// Head input of depth 1, one workgroup per sequence: y[s] = bf16(h[s] +
+// e[root[s]]), 16-byte pieces added in float and rounded once.  Tokens outside
 // [0, V) are clamped into it, so every read stays inside e.
 __global__ __launch_bounds__(256) void hydra_embed(const uint16_t* __restrict__ h,
                                                    const uint16_t* __restrict__ E,
-                                                   const int* __restrict__ root,
-                                                   const int* __restrict__ tokens, int T, int H,
-                                                   int V, int first, int n, bool from_root,
+                                                   const int* __restrict__ root, int H, int V,
                                                    uint16_t* __restrict__ y) {
-  const int r = blockIdx.x;
-  const int s = r / n, j = r - s * n;
-  int tok = from_root ? root[s] : tokens[(int64_t)s * T + first + j];
+  const int r = blockIdx.x, s = r;
+  int tok = root[s];
   tok = min(max(tok, 0), V - 1);
   const uint4* hp = reinterpret_cast<const uint4*>(h + (int64_t)s * H);
   const uint4* ep = reinterpret_cast<const uint4*>(E + (int64_t)tok * H);
@@ -57,17 +56,36 @@ __global__ __launch_bounds__(256) void hydra_embed(const uint16_t* __restrict__ 
   }
 }
 
-// One thread per (sequence, node of depth d): the node's token is rank r of
-// its parent's shortlist, idx row s * n_par + (parent - first_par).
-__global__ __launch_bounds__(256) void hydra_children(const int* __restrict__ idx, int kmax,
-                                                      TreeDev t, int first, int nchild,
-                                                      int first_par, int n_par, int b,
-                                                      int* __restrict__ tokens) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= b * nchild) return;
-  const int s = g / nchild, c = first + (g - s * nchild);
+// One workgroup per (sequence, node c of depth d), row r = s * nchild + (c -
+// first): c's token is rank r_c of its parent's shortlist (idx row s * n_par +
+// (parent - first_par)); when a deeper depth follows (y != nullptr) the same
+// workgroup also writes c's row of the next depth's head input,
+// y[r] = bf16(h[s] + e[token]), as hydra_embed does for the root.
+__global__ __launch_bounds__(256) void hydra_next(const int* __restrict__ idx, int kmax,
+                                                  TreeDev t, int first, int nchild, int first_par,
+                                                  int n_par, const uint16_t* __restrict__ h,
+                                                  const uint16_t* __restrict__ E, int H, int V,
+                                                  int* __restrict__ tokens,
+                                                  uint16_t* __restrict__ y) {
+  const int r = blockIdx.x;
+  const int s = r / nchild, c = first + (r - s * nchild);
   const int p = t.parent[c];
-  tokens[(int64_t)s * t.T + c] = idx[((int64_t)s * n_par + (p - first_par)) * kmax + t.rank[c]];
+  int tok = idx[((int64_t)s * n_par + (p - first_par)) * kmax + t.rank[c]];
+  if (threadIdx.x == 0) tokens[(int64_t)s * t.T + c] = tok;
+  if (y == nullptr) return;
+  tok = min(max(tok, 0), V - 1);
+  const uint4* hp = reinterpret_cast<const uint4*>(h + (int64_t)s * H);
+  const uint4* ep = reinterpret_cast<const uint4*>(E + (int64_t)tok * H);
+  uint4* yp = reinterpret_cast<uint4*>(y + (int64_t)r * H);
+  for (int q = threadIdx.x; q < H / 8; q += blockDim.x) {
+    const uint4 a = hp[q], e = ep[q];
+    uint4 o;
+    o.x = pack_bf16x2(bf16_lo(a.x) + bf16_lo(e.x), bf16_hi(a.x) + bf16_hi(e.x));
+    o.y = pack_bf16x2(bf16_lo(a.y) + bf16_lo(e.y), bf16_hi(a.y) + bf16_hi(e.y));
+    o.z = pack_bf16x2(bf16_lo(a.z) + bf16_lo(e.z), bf16_hi(a.z) + bf16_hi(e.z));
+    o.w = pack_bf16x2(bf16_lo(a.w) + bf16_lo(e.w), bf16_hi(a.w) + bf16_hi(e.w));
+    yp[q] = o;
+  }
 }
 
 // logits_out rows (s, first + j) <- parent row r = s * n + j of the pass
@@ -144,11 +162,12 @@ hipError_t run_hydra_draft(const void* h, const void* E, const void* W, const vo
   for (int d = 1; d <= hs.D; ++d) {
     const int n = hs.n[d - 1], first = hs.first[d - 1];
     const int rows = b * n;
-    hipLaunchKernelGGL(hydra_embed, dim3(rows), dim3(256), 0, st, static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(E), root, o.tokens, t.T, H, V, first, n,
-                       d == 1, y);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (d == 1) {
+      hipLaunchKernelGGL(hydra_embed, dim3(b), dim3(256), 0, st, static_cast<const uint16_t*>(h),
+                         static_cast<const uint16_t*>(E), root, H, V, y);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     e = run_heads_hidden(y, rows, H, Wb + (size_t)(d - 1) * H * H, 1, kBF16, u, 1, 0, st);
     if (e != hipSuccess) return e;
     // consecutive passes walk the weights' K chunks in opposite directions, so
@@ -167,9 +186,11 @@ hipError_t run_hydra_draft(const void* h, const void* E, const void* W, const vo
     q.k[0] = a.k[d - 1];
     e = run_topk(lg, q, nullptr, idx, val, tws, st);
     if (e != hipSuccess) return e;
+    // the children's tokens and, below the deepest depth, their head inputs
     const int nchild = hs.n[d];
-    hipLaunchKernelGGL(hydra_children, dim3((b * nchild + 255) / 256), dim3(256), 0, st, idx, kmax,
-                       t, hs.first[d], nchild, first, n, b, o.tokens);
+    hipLaunchKernelGGL(hydra_next, dim3(b * nchild), dim3(256), 0, st, idx, kmax, t, hs.first[d],
+                       nchild, first, n, static_cast<const uint16_t*>(h),
+                       static_cast<const uint16_t*>(E), H, V, o.tokens, d < hs.D ? y : nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
