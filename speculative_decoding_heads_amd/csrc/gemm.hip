@@ -589,6 +589,7 @@ struct Bf16Plan {
   int nw;        // tiled: waves per workgroup
   int wmb, wnb;  // ring: tile parameters
   int ntiles;    // workgroup tiles along N
+  int snb;       // skinny: 16-row weight blocks per workgroup (1 or 2)
 };
 
 static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
@@ -598,9 +599,20 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
   // every CU one, they stream best; otherwise skinny (up to 16 rows) or
   // 4-wave tiled workgroups keep more of them in flight.
   const bool wide = N >= 240 * 128;
-  if (skinny_ok && !wide && M <= 16) {
+  if (skinny_ok && !wide && M <= 16 && N >= 256 * 32) {
     p.kind = 0;
+    p.snb = 2;
+    p.mb = 1;
     p.ntiles = (N + 31) / 32;
+    return p;
+  }
+  // a single head (N = H): 16-row weight blocks so that the launch still has
+  // about one workgroup per CU, up to 32 activation rows per workgroup
+  if (skinny_ok && M <= 32 && N < 256 * 32) {
+    p.kind = 0;
+    p.snb = 1;
+    p.mb = mb;
+    p.ntiles = (N + 15) / 16;
     return p;
   }
   if (logits && mb > 5 && (Kd % 64) == 0) {
@@ -650,8 +662,15 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
   const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
   if (p.kind == 0) {
     // skinny: 4 waves split K, X (a few rows) read from L2
-    hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx, M,
-                       W, N, Kd, epi);
+    if (p.snb == 2)
+      hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
+                         M, W, N, Kd, epi);
+    else if (p.mb == 1)
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
+                         M, W, N, Kd, epi);
+    else
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 2, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
+                         M, W, N, Kd, epi);
     return hipGetLastError();
   }
   if constexpr (IsLogits<Epi>::value) if (p.kind == 2) {
