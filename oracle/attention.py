@@ -112,3 +112,24 @@ def attention_row(q, Kc_sg, Vc_sg, P, anc_row, scale):
     K = np.asarray(Kc_sg[: P + T], dtype=np.float64)[vis]
     V = np.asarray(Vc_sg[: P + T], dtype=np.float64)[vis]
     return _softmax_attend(np.asarray(q, dtype=np.float64), K, V, scale)
+
+
+def tree_attention_head(q, Kc_sg, Vc_sg, P, anc, scale):
+    """Every node of one q head at once, as masked attention over a score matrix.
+
+    q: [T, d] (the head's query of each node); Kc_sg, Vc_sg: [>= P+T, d] (the
+    head's kv-head cache); anc: [T, T] bool.  S = scale * q K^T over all P+T
+    keys, keys a node may not see set to -inf (prefix always visible, tree slot
+    P+j visible iff anc[t, j]), row softmax, times V.  Returns [T, d] float64.
+    The same quantity as tree_attention, written as one masked matrix product
+    rather than a gather of the visible rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T = q.shape[0]
+    K = np.asarray(Kc_sg[: P + T], dtype=np.float64)
+    V = np.asarray(Vc_sg[: P + T], dtype=np.float64)
+    vis = np.concatenate([np.ones((T, P), dtype=bool), np.asarray(anc, dtype=bool)], axis=1)
+    S = np.where(vis, (q @ K.T) * scale, -np.inf)
+    S = S - S.max(axis=1, keepdims=True)
+    E = np.exp(S)
+    return (E @ V) / E.sum(axis=1, keepdims=True)

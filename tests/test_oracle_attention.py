@@ -105,3 +105,25 @@ def test_sampled_row_helper_matches_batch_routine():
     for t in range(plan.T):
         r = attention_row(Q[0, t, 1], Kc[0, 0], Vc[0, 0], 6, plan.anc[t], 1 / np.sqrt(8))
         assert np.allclose(r, O[t, 1], atol=1e-14)
+
+
+@settings(max_examples=30, deadline=None)
+@given(k=st.lists(st.integers(1, 4), min_size=1, max_size=3), frac=st.floats(0.0, 1.0),
+       P=st.integers(0, 12), heads=st.sampled_from([(2, 2), (4, 2), (6, 3)]),
+       seed=st.integers(0, 10 ** 6))
+def test_head_matrix_form_equals_per_path_causal(k, frac, P, heads, seed):
+    # the score-matrix form used by the full-size checks (one q head, every
+    # node) must equal the brute-force per-path causal attention
+    from oracle import full_tree_node_count
+    from oracle.attention import tree_attention_head
+    N = int(round(frac * full_tree_node_count(k)))
+    plan = tree_plan(k, N)
+    nq, nkv = heads
+    d = 8
+    Q, Kc, Vc = _inputs(1, plan.T, nq, nkv, d, P, seed)
+    ref = path_attention(Q, Kc, Vc, [P], plan.parent).reshape(plan.T, nq, d)
+    G = nq // nkv
+    for hq in range(nq):
+        got = tree_attention_head(Q[0, :, hq], Kc[0, hq // G], Vc[0, hq // G], P, plan.anc,
+                                  1 / np.sqrt(d))
+        assert np.allclose(got, ref[:, hq], rtol=1e-12, atol=1e-12)

@@ -187,3 +187,30 @@ def test_sampler_peaked_and_edges():
     assert sample_tempered(row, 1.0, 0.0)[0] == 0
     assert sample_tempered(row, 1.0, 1.0 - 2.0 ** -24)[0] == 7
     assert sample_tempered(row, 1.0, 0.5)[0] == 4        # running sum 5 > 4
+
+
+def test_counter_layout_lands_on_published_outputs():
+    # Pin the counter layout seed ^ step<<32 ^ seq<<8 ^ draw against the
+    # published SplitMix64 outputs: the n-th output of the stream from state 0
+    # is splitmix64(n * gamma), so (seed, step, seq, draw) chosen to XOR to
+    # n * gamma must give the golden output's top 24 bits.  The second case
+    # overlaps draw with seq << 8, so OR in place of XOR fails it, as would
+    # step << 31 or a >> 41.
+    with open(os.path.join(GOLD, "splitmix64_state0.txt")) as f:
+        gold = [int(ln, 16) for ln in f if ln.strip() and not ln.startswith("#")]
+    gamma, mask = 0x9E3779B97F4A7C15, (1 << 64) - 1
+    # output 2: counter 2 * gamma = 0x3C6EF372_FE94F82A, split over the fields
+    two = (2 * gamma) & mask
+    assert two == 0x3C6EF372FE94F82A
+    assert counter_uniform(0, 0x3C6EF372, 0xFE94F8, 0x2A) == (gold[2] >> 40) * 2.0 ** -24
+    # output 3: counter 3 * gamma, with a seed bit cancelled by step and a draw
+    # bit (bit 8) cancelled by seq
+    three = (3 * gamma) & mask
+    hi, lo = three >> 32, three & 0xFFFFFFFF
+    seed = 1 << 32
+    step = hi ^ 1
+    draw = (lo & 0xFF) ^ 0x100
+    seq = (lo >> 8) ^ 1
+    assert (seed ^ (step << 32) ^ (seq << 8) ^ draw) & mask == three
+    assert counter_uniform(seed, step, seq, draw) == (gold[3] >> 40) * 2.0 ** -24
+    assert gold[3] >> 40 == 0xF88BB8
