@@ -103,6 +103,29 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
                  float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * medusa_heads_hidden / medusa_lm_logits - the two halves of medusa_heads as
+ * calls of their own (the same kernels; each call is one GEMM), for callers
+ * that schedule or time them apart.  [deep-dive] "The heads are residual
+ * blocks, not linear layers": the residual block, then the shared LM
+ * projection.
+ *
+ * medusa_heads_hidden: u_out [rows, R, H] (dtype), R = include_base + n_heads
+ *   (n_heads >= 1): slot 0 = x when include_base, then x + SiLU(W_i x)
+ *   rounded to dtype, exactly as medusa_heads writes u_out.
+ * medusa_lm_logits: logits [rows, V] f32 = x [rows, H] . LM^T.  reverse_k = 1
+ *   sums the K chunks in the order medusa_heads uses for head rows, 0 in the
+ *   order it uses with n_heads = 0 (verify rows).
+ * medusa_heads(x, W, n_heads > 0, ..., u_out, logits) is bit for bit
+ * medusa_heads_hidden(x, ..., u_out) then medusa_lm_logits(u_out viewed as
+ * [rows * R, H], reverse_k = 1); with n_heads = 0 it is medusa_lm_logits(x,
+ * reverse_k = 0).  Requirements and errors as medusa_heads.
+ * ------------------------------------------------------------------------- */
+int medusa_heads_hidden(const void* x, int64_t rows, int32_t H, const void* W, int32_t n_heads,
+                        int32_t dtype, int32_t include_base, void* u_out, void* stream);
+int medusa_lm_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
+                     int32_t dtype, int32_t reverse_k, float* logits, void* stream);
+
+/* ---------------------------------------------------------------------------
  * medusa_topk - per-head shortlists and the root token.
  * [deep-dive] "From top-k heads to a sparse candidate tree": keep the top k_i
  * tokens of head i.  Order: logit descending, equal logits by the lower
@@ -274,8 +297,11 @@ int medusa_kv_compact(void* Kc, void* Vc, int32_t* seq_len, const int32_t* path,
  * softmax statistics come from its partials instead of a pass over
  * base_logits.  The statistics then differ only in float32 rounding, so the
  * outputs are the same except for a node whose typical-acceptance margin is
- * within that rounding.  Errors: the union of both calls' checks; nothing is
- * launched on error.
+ * within that rounding.  The partials carry a record of the call that made
+ * them (rows, V, greedy keys or tempered statistics, temperature); when it
+ * does not match this call the kernel reads base_logits instead (slower, and
+ * never past the partials).  Errors: the union of both calls' checks; nothing
+ * is launched on error.
  * ------------------------------------------------------------------------- */
 int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const int32_t* parent,
                           const int32_t* depth, int32_t b, int32_t T, int32_t V, int32_t K,

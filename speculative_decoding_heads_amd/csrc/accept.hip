@@ -156,19 +156,32 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats(const float* __rest
 
 // The same statistics from the verify GEMM's per-tile partials: one wave per
 // node row; each lane merges tiles lane, lane + 64, ... (four in flight), then
-// the wave reduces its lanes.
+// the wave reduces its lanes.  The partials are used only when their header
+// says they were made for this call (rows, vocabulary, kind of statistics and
+// temperature); otherwise the wave folds the logits row itself, so a
+// mismatched workspace gives the statistics of the logits, never a read past
+// the partials.
 template <int MODE>
 __global__ __launch_bounds__(256) void accept_parts(const int* __restrict__ hdr,
                                                     const uint64_t* __restrict__ pkey,
                                                     const RowStat* __restrict__ pstat, int rows,
-                                                    int* __restrict__ amax,
+                                                    const float* __restrict__ logits, int V,
+                                                    float inv_temp, int* __restrict__ amax,
                                                     RowStat* __restrict__ stats) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int ntiles = hdr[0];
+  const bool typ = MODE == kTypical;
+  const bool match = hdr[kHdrMagic] == kPartsMagic && hdr[kHdrRows] == rows &&
+                     hdr[kHdrCols] == V && hdr[kHdrKind] == (typ ? 1 : 0) &&
+                     hdr[kHdrTiles] >= 1 && (!typ || hdr[kHdrInvTemp] == __float_as_int(inv_temp));
+  const int ntiles = match ? hdr[kHdrTiles] : 0;
   RowPart acc;
   part_init(acc);
+  if (!match) {
+    const float* x = logits + (int64_t)row * V;
+    for (int e = lane; e < V; e += 64) part_add(acc, x[e], e, typ, inv_temp);
+  }
   for (int j0 = 0; j0 < ntiles; j0 += 4 * 64) {
     RowPart q[4];
 #pragma unroll
@@ -405,7 +418,7 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   if (mode == kGreedy) {
     if (parts)
       hipLaunchKernelGGL(accept_parts<kGreedy>, dim3(pgrid), dim3(256), 0, st, hdr, pkey, pstat,
-                         (int)rows, amax, stats);
+                         (int)rows, base_logits, V, inv_temp, amax, stats);
     else
       hipLaunchKernelGGL(accept_stats<kGreedy>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
                          base_logits, V, inv_temp, amax, stats);
@@ -418,7 +431,7 @@ hipError_t run_accept(const float* base_logits, const int* tokens, const int* pa
   // typical and rejection modes: tempered statistics of every node row
   if (parts)
     hipLaunchKernelGGL(accept_parts<kTypical>, dim3(pgrid), dim3(256), 0, st, hdr, pkey, pstat,
-                       (int)rows, amax, stats);
+                       (int)rows, base_logits, V, inv_temp, amax, stats);
   else
     hipLaunchKernelGGL(accept_stats<kTypical>, dim3((unsigned)rows), dim3(kStatThreads), 0, st,
                        base_logits, V, inv_temp, amax, stats);

@@ -113,6 +113,46 @@ int medusa_heads(const void* x, int64_t rows, int32_t H, const void* W, int32_t 
                     "LM projection");
 }
 
+int medusa_heads_hidden(const void* x, int64_t rows, int32_t H, const void* W, int32_t n_heads,
+                        int32_t dtype, int32_t include_base, void* u_out, void* stream) {
+  if (rows < 0) return fail(MEDUSA_ERR_ARG, "rows < 0");
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (H <= 0) return fail(MEDUSA_ERR_ARG, "H must be positive");
+  if (n_heads < 1 || n_heads > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "n_heads out of range [1, 16]");
+  if (include_base != 0 && include_base != 1) return fail(MEDUSA_ERR_ARG, "include_base must be 0 or 1");
+  const int R = include_base + n_heads;
+  if (rows == 0) return MEDUSA_OK;
+  if (!x || !W || !u_out) return fail(MEDUSA_ERR_ARG, "x, W and u_out must be non-NULL");
+  if (rows * R > INT32_MAX / 2 || (int64_t)n_heads * H > INT32_MAX / 2)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "too many rows");
+  if (dtype == MEDUSA_BF16) {
+    if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "bf16 heads need H % 128 == 0");
+    if (!aligned16(x) || !aligned16(W) || !aligned16(u_out))
+      return fail(MEDUSA_ERR_ARG, "bf16 operands must be 16-byte aligned");
+  }
+  return hip_status(run_heads_hidden(x, (int)rows, H, W, n_heads, dtype, u_out, R, include_base,
+                                     as_stream(stream)),
+                    "heads hidden");
+}
+
+int medusa_lm_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
+                     int32_t dtype, int32_t reverse_k, float* logits, void* stream) {
+  if (rows < 0) return fail(MEDUSA_ERR_ARG, "rows < 0");
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_ARG, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+  if (H <= 0 || V <= 0) return fail(MEDUSA_ERR_ARG, "H and V must be positive");
+  if (reverse_k != 0 && reverse_k != 1) return fail(MEDUSA_ERR_ARG, "reverse_k must be 0 or 1");
+  if (rows == 0) return MEDUSA_OK;
+  if (!x || !LM || !logits) return fail(MEDUSA_ERR_ARG, "x, LM and logits must be non-NULL");
+  if (rows > INT32_MAX / 2) return fail(MEDUSA_ERR_UNSUPPORTED, "too many rows");
+  if (dtype == MEDUSA_BF16) {
+    if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "bf16 rows need H % 128 == 0");
+    if (!aligned16(x) || !aligned16(LM)) return fail(MEDUSA_ERR_ARG, "bf16 operands must be 16-byte aligned");
+  }
+  return hip_status(run_lm_logits(x, (int)rows, H, LM, V, dtype, logits, as_stream(stream),
+                                  reverse_k == 1),
+                    "LM projection");
+}
+
 // ------------------------------------------------------------------- verify logits + partials
 size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode) {
   if (rows <= 0 || H <= 0 || V <= 0 || !dtype_ok(dtype)) return 0;

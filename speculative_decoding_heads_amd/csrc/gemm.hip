@@ -78,9 +78,12 @@ struct EpiLogitsStats : EpiLogits {
   }
   __device__ __forceinline__ void write_header() const {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-      header[0] = ntiles;
-      header[1] = typical ? 1 : 0;
-      header[2] = M;
+      header[kHdrTiles] = ntiles;
+      header[kHdrKind] = typical ? 1 : 0;
+      header[kHdrRows] = M;
+      header[kHdrCols] = N;
+      header[kHdrInvTemp] = __float_as_int(inv_temp);
+      header[kHdrMagic] = kPartsMagic;
     }
   }
 };
@@ -794,9 +797,12 @@ __global__ __launch_bounds__(256) void row_parts_f32(const float* __restrict__ l
     if (typical) pstat[row] = RowStat{pt.m, pt.s, pt.t, 0.f};
     else pkey[row] = pt.key;
     if (row == 0) {
-      header[0] = 1;
-      header[1] = typical ? 1 : 0;
-      header[2] = M;
+      header[kHdrTiles] = 1;
+      header[kHdrKind] = typical ? 1 : 0;
+      header[kHdrRows] = M;
+      header[kHdrCols] = V;
+      header[kHdrInvTemp] = __float_as_int(inv_temp);
+      header[kHdrMagic] = kPartsMagic;
     }
   }
 }

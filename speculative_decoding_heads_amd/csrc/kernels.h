@@ -25,9 +25,13 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
                          float* logits, hipStream_t st, bool rev = false, int64_t ldc = 0);
 // LM projection of the verify rows plus acceptance partials per (row, weight
-// tile) in ws: header (kPartsHeader bytes: ntiles, typical, rows), then
-// [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).
+// tile) in ws: a header (kPartsHeader bytes, the int32 fields below), then
+// [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).  The header
+// records what the partials were made for; acceptance uses them only when
+// every field matches its own call (else it reads the logits).
 constexpr size_t kPartsHeader = 256;
+enum { kHdrTiles = 0, kHdrKind = 1, kHdrRows = 2, kHdrCols = 3, kHdrInvTemp = 4, kHdrMagic = 5 };
+constexpr int kPartsMagic = 0x4D445653;
 int verify_tiles(int M, int N, int Kd, int dtype);
 // whether run_verify_logits leaves partials (else acceptance reads the logits)
 bool verify_uses_parts(int64_t M, int64_t N);

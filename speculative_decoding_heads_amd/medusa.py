@@ -45,6 +45,8 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_heads_workspace": ([_I64, _I32, _I32, _I32, _I32], _SZ),
     "medusa_heads": ([_P, _I64, _I32, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "medusa_heads_hidden": ([_P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P], _I32),
+    "medusa_lm_logits": ([_P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P], _I32),
     "medusa_topk_workspace": ([_I32, _I32, _I32, _I32], _SZ),
     "medusa_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _F, _U64, _U64, _P, _P, _P, _P, _SZ,
                      _P], _I32),
@@ -197,6 +199,35 @@ def medusa_heads(x, W, LM, logits, include_base=1, u_out=None, ws=None, stream=N
                             include_base, _ptr(u_out), _ptr(logits), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream(stream))
     _check("medusa_heads", st)
+
+
+def medusa_heads_hidden(x, W, u_out, include_base=1, stream=None):
+    """u_out [rows, include_base + K, H]: the residual blocks of medusa_heads."""
+    rows, H = x.shape
+    n_heads = W.shape[0]
+    _shape(W, (n_heads, H, H), "W")
+    _dt(W, x.dtype, "W")
+    R = (1 if include_base else 0) + n_heads
+    _need(u_out.numel() == rows * R * H and u_out.shape[-1] == H, "u_out: expected rows*R*H entries")
+    _dt(u_out, x.dtype, "u_out")
+    st = lib().medusa_heads_hidden(_ptr(x), rows, H, _ptr(W), n_heads, dtype_code(x),
+                                   include_base, _ptr(u_out), _stream(stream))
+    _check("medusa_heads_hidden", st)
+
+
+def medusa_lm_logits(x, LM, logits, reverse_k=0, stream=None):
+    """logits [rows, V] = x [rows, H] . LM^T (x may be any view with rows of H)."""
+    H = x.shape[-1]
+    rows = x.numel() // H
+    V = LM.shape[0]
+    _shape(LM, (V, H), "LM")
+    _dt(LM, x.dtype, "LM")
+    _need(x.is_contiguous(), "x must be contiguous")
+    _need(logits.numel() == rows * V and logits.shape[-1] == V, "logits: expected rows*V entries")
+    _dt(logits, torch.float32, "logits")
+    st = lib().medusa_lm_logits(_ptr(x), rows, H, _ptr(LM), V, dtype_code(x), int(reverse_k),
+                                _ptr(logits), _stream(stream))
+    _check("medusa_lm_logits", st)
 
 
 def _topk_shapes(logits, k, kmax, root, idx, val):

@@ -5,6 +5,7 @@ library calls in loop order (inferensys.com "Medusa Heads": draft, verify,
 accept and roll back); every part of the step runs in the HIP kernels.
 
     heads      : medusa_heads(h)            -> logits [b, K+1, V]
+                 (fused: medusa_heads_hidden + medusa_lm_logits, the same kernels)
     shortlists : medusa_topk(logits)        -> root [b], idx [b, K, kmax]
     tree       : medusa_build_tree          -> tokens, pos, parent, depth, anc
     verify     : medusa_tree_attn(Q, Kc, Vc)-> O [b, T, nq*d]
@@ -101,10 +102,16 @@ class VerifyStep:
         self.verify(x, step, fused, stream)
 
     def draft_medusa(self, x, step, root_mode, root, fused, stream=None):
-        """The Medusa draft of one step: head logits, root, shortlists and tree."""
+        """The Medusa draft of one step: head logits, root, shortlists and tree.
+        Fused path: the heads' residual GEMM and their LM pass as two calls
+        (medusa_heads_hidden, medusa_lm_logits: the kernels of medusa_heads)."""
         c = self.cfg
-        M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
-                       stream=stream)
+        if fused:
+            M.medusa_heads_hidden(x["h"], x["W"], self.u, include_base=1, stream=stream)
+            M.medusa_lm_logits(self.u, x["LM"], self.logits, reverse_k=1, stream=stream)
+        else:
+            M.medusa_heads(x["h"], x["W"], x["LM"], self.logits, include_base=1, u_out=self.u,
+                           stream=stream)
         if fused and self.plan is not None:
             M.medusa_topk_tree_tables(self.logits, c.k, c.kmax, self.plan[0], self.plan[1],
                                       root_mode, c.temperature, c.seed, step, x["seq_len"], root,

@@ -305,3 +305,24 @@ def test_hydra_draft_argument_checks():
     need = M.medusa_hydra_workspace(1, 256, 100, [4, 3], 4, list(par), list(rk))
     assert need > 0 and need % 256 == 0
     assert M.medusa_hydra_workspace(2, 256, 100, [4, 3], 4, list(par), list(rk)) > need
+
+
+def test_split_heads_argument_checks():
+    """medusa_heads_hidden / medusa_lm_logits (the halves of medusa_heads)
+    validate before any launch; empty batches are no-ops."""
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # heads hidden: n_heads 0, unaligned, H % 128, NULL u_out, bad include_base
+    assert L.medusa_heads_hidden(fake, 1, 128, fake, 0, M.BF16, 1, fake, None) == ERR_ARG
+    assert L.medusa_heads_hidden(ctypes.c_void_p(0x1002), 1, 128, fake, 2, M.BF16, 1, fake,
+                                 None) == ERR_ARG
+    assert L.medusa_heads_hidden(fake, 1, 100, fake, 2, M.BF16, 1, fake, None) == ERR_UNSUPPORTED
+    assert L.medusa_heads_hidden(fake, 1, 128, fake, 2, M.BF16, 1, None, None) == ERR_ARG
+    assert L.medusa_heads_hidden(fake, 1, 128, fake, 2, M.BF16, 2, fake, None) == ERR_ARG
+    assert L.medusa_heads_hidden(None, 0, 128, None, 2, M.BF16, 1, None, None) == 0
+    # LM projection: reverse flag, H % 128, dtype, NULL logits
+    assert L.medusa_lm_logits(fake, 1, 128, fake, 10, M.BF16, 2, fake, None) == ERR_ARG
+    assert L.medusa_lm_logits(fake, 1, 100, fake, 10, M.BF16, 0, fake, None) == ERR_UNSUPPORTED
+    assert L.medusa_lm_logits(fake, 1, 128, fake, 10, 5, 0, fake, None) == ERR_ARG
+    assert L.medusa_lm_logits(fake, 1, 128, fake, 10, M.BF16, 1, None, None) == ERR_ARG
+    assert L.medusa_lm_logits(None, 0, 128, None, 10, M.BF16, 1, None, None) == 0

@@ -29,12 +29,15 @@ def _gpu():
 
 # ------------------------------------------------------------------ heads
 HEAD_CASES = [
-    # b, H, V, K, dtype
-    (1, 128, 1000, 4, "bf16"),     # skinny, one 16-row block, ragged vocab tile
+    # b, H, V, K, dtype   (comments: the head GEMM / the LM projection)
+    (1, 128, 1000, 4, "bf16"),     # skinny 1-block; one 16-row block, ragged vocab tile
     (3, 256, 4093, 2, "bf16"),     # V % 4 != 0: scalar logit stores
-    (17, 384, 2048, 1, "bf16"),    # 3 K-chunks (odd), 34 rows: 4-wave tiled
-    (16, 256, 3000, 4, "bf16"),    # 80 rows
-    (40, 256, 1000, 4, "bf16"),    # 200 rows: tiled kernel, ragged M and N tiles
+    (17, 384, 2048, 1, "bf16"),    # N = H < 8192, 17 rows: 16-row skinny workgroups with
+                                   # two row blocks; 3 K-chunks (odd); 34 LM rows
+    (16, 256, 3000, 4, "bf16"),    # N = 1024, 16 rows: skinny, one row block; 80 LM rows
+    (32, 256, 1000, 1, "bf16"),    # N = H, 32 rows: the last row count on skinny workgroups
+    (33, 256, 1000, 1, "bf16"),    # N = H, 33 rows: the first on the tiled kernel
+    (40, 256, 1000, 4, "bf16"),    # 200 LM rows: tiled kernel, ragged M and N tiles
     (3, 2048, 1000, 16, "bf16"),   # 32768 head rows: 8-wave tiled, rotated K walk
     (1, 256, 4096, 3, "f32"),      # tiny fp32 workload shape
     (5, 100, 777, 2, "f32"),
@@ -365,16 +368,22 @@ def test_accept_typical_exact(k, N, V, scale):
     toks, xs = zip(*[_plant(plan, V, rng, 0.5, scale) for _ in range(b)])
     tokens, x = np.stack(toks), np.stack(xs)
     L, path, acc, bonus = _accept_run(x, tokens, plan, K, M.TYPICAL, T_=Tf, seed=77, step=2)
+    compared = bonus_compared = 0
     for s in range(b):
         r = accept_typical(x[s], tokens[s], plan.parent, plan.depth, K, Tf, 0.3, 0.09, 77, 2, s)
         guarded = np.min(r[4][1:]) < 1e-4
         if not guarded:
             assert L[s] == r[0] and list(path[s]) == list(r[1]) and list(acc[s]) == list(r[2])
+            compared += 1
             best = r[1][r[0]]
             u = counter_uniform(77, 2, s, 1)
             want, c = sample_tempered(x[s, best], Tf, u)
             if np.min(np.abs(c - u * c[-1])) / c[-1] > 1e-12:
                 assert bonus[s] == want == r[3]
+                bonus_compared += 1
+    # on these seeds no decision or draw lies within the guard bands (the
+    # oracle alone decides that), so every sequence must have been compared
+    assert compared == b and bonus_compared == b, (compared, bonus_compared)
 
 
 def test_accept_typical_eps_branch():
