@@ -28,7 +28,9 @@
  *     leaves the cache untouched in compaction; out-of-range tokens are
  *     rejected by acceptance.
  *   - Calls are reentrant.  The only library state is an immutable cache of
- *     tree plans keyed by (k, N, decay), guarded by a mutex.
+ *     tree plans keyed by (k, N, decay), guarded by a mutex, and the static
+ *     device scratch of medusa_tree_attn_noalloc (one array per GPU, shared by
+ *     every call of that entry point on the GPU).
  *   - Calls that share buffers must be ordered on one stream by the caller.
  */
 #ifndef MEDUSA_H
@@ -227,6 +229,27 @@ int medusa_tree_attn(const void* Q, const void* Kc, const void* Vc, const int32_
                      const uint64_t* anc, int32_t anc_words, int32_t b, int32_t T, int32_t nq,
                      int32_t nkv, int32_t d, int32_t Pmax, float scale, int32_t dtype, void* O,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * medusa_tree_attn_noalloc - medusa_tree_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, checks, kernels and outputs as
+ * medusa_tree_attn, without the workspace: the split-KV partials live in a
+ * static device array of MEDUSA_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends (its address is looked up on
+ * the first call on a device, with that device current; the stream must
+ * belong to the current device).  The call allocates and frees nothing.
+ * Shapes whose partials (medusa_tree_attn_workspace bytes) exceed the array
+ * return MEDUSA_ERR_UNSUPPORTED and launch nothing.  Every call on a GPU
+ * shares that GPU's array and leaves its partials there: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  Nothing in the array needs to start at zero.
+ * ------------------------------------------------------------------------- */
+#define MEDUSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int medusa_tree_attn_noalloc(const void* Q, const void* Kc, const void* Vc,
+                             const int32_t* seq_len, const uint64_t* anc, int32_t anc_words,
+                             int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d,
+                             int32_t Pmax, float scale, int32_t dtype, void* O, void* stream);
 
 /* ---------------------------------------------------------------------------
  * medusa_accept - acceptance, the accepted path and the next token.

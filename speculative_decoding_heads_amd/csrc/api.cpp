@@ -486,6 +486,36 @@ int medusa_tree_attn(const void* Q, const void* Kc, const void* Vc, const int32_
                     "tree_attn");
 }
 
+static_assert(MEDUSA_NOALLOC_SCRATCH_BYTES == kAttnScratchBytes,
+              "the header states the size of the static scratch");
+
+int medusa_tree_attn_noalloc(const void* Q, const void* Kc, const void* Vc,
+                             const int32_t* seq_len, const uint64_t* anc, int32_t anc_words,
+                             int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d,
+                             int32_t Pmax, float scale, int32_t dtype, void* O, void* stream) {
+  if (int s = attn_check(b, T, nq, nkv, d, Pmax, dtype)) return s;
+  if (anc_words < (T + 63) / 64 || anc_words > MEDUSA_MAX_T / 64)
+    return fail(MEDUSA_ERR_ARG, "anc_words must be in [ceil(T/64), 4]");
+  if (!std::isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale must be finite");
+  if (b == 0) return MEDUSA_OK;
+  if (!Q || !Kc || !Vc || !seq_len || !anc || !O) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (dtype == MEDUSA_BF16 && (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O)))
+    return fail(MEDUSA_ERR_ARG, "bf16 attention operands must be 16-byte aligned");
+  AttnPlan p = attn_plan(b, T, nq, nkv, d, Pmax, dtype);
+  if (p.ws_bytes > attn_scratch_bytes())
+    return fail(MEDUSA_ERR_UNSUPPORTED,
+                "tree_attn_noalloc: the split-KV partials of this shape exceed the "
+                "MEDUSA_NOALLOC_SCRATCH_BYTES of static scratch");
+  void* ws = nullptr;
+  if (p.ws_bytes) {
+    hipError_t e = attn_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "tree_attn_noalloc (scratch address)");
+  }
+  return hip_status(run_tree_attn(Q, Kc, Vc, seq_len, anc, anc_words, b, T, nq, nkv, d, Pmax, scale,
+                                  dtype, O, ws, p, as_stream(stream)),
+                    "tree_attn_noalloc");
+}
+
 // ------------------------------------------------------------------- accept
 size_t medusa_accept_workspace(int32_t b, int32_t T) {
   if (b <= 0 || T <= 0) return 0;

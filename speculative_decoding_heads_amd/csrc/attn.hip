@@ -31,6 +31,7 @@
 // f32 kernel (tiny fp32 workload): one workgroup per (sequence, node, q head),
 // scores staged in LDS, exact two-pass softmax.
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -525,6 +526,40 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
     hipLaunchKernelGGL(attn_merge<64>, dim3((rows + 15) / 16, b * nkv), dim3(256), 0, st, ws_o,
                        ws_ml, p.nsplit, rows, rows_pad, T, nq, nkv, o);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// medusa_tree_attn_noalloc keeps the split-KV partials in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, so its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// passed to kernels.  Nothing in it needs to start at zero: every partial
+// (output rows and (max, sum) pairs) is written by the attention kernel before
+// attn_merge reads it.  Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+hipError_t attn_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace medusa

@@ -113,6 +113,11 @@ struct AttnPlan {
   int tiles_per_split;  // 64-key tiles per partition
 };
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
+// the static scratch of the no-allocation attention call: its size, and its
+// device address on the current device (looked up once per device)
+constexpr size_t kAttnScratchBytes = size_t(16) << 20;
+size_t attn_scratch_bytes();
+hipError_t attn_scratch(void** out);
 hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const int* seq_len,
                          const uint64_t* anc, int anc_words, int b, int T, int nq, int nkv, int d,
                          int Pmax, float scale, int dtype, void* O, void* ws, const AttnPlan& p,

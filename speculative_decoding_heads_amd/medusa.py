@@ -56,6 +56,8 @@ _SIGS = {
     "medusa_tree_attn_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "medusa_tree_attn": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _I32,
                           _P, _P, _SZ, _P], _I32),
+    "medusa_tree_attn_noalloc": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                  _F, _I32, _P, _P], _I32),
     "medusa_accept_workspace": ([_I32, _I32], _SZ),
     "medusa_accept": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _F, _F, _U64, _U64, _P, _P,
                        _P, _P, _P, _SZ, _P], _I32),
@@ -343,6 +345,27 @@ def medusa_tree_attn(Q, Kc, Vc, seq_len, anc, O, scale=None, ws=None, stream=Non
                                 b, T, nq, nkv, d, Pmax, scale, dtype_code(Q), _ptr(O), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(stream))
     _check("medusa_tree_attn", st)
+
+
+def medusa_tree_attn_noalloc(Q, Kc, Vc, seq_len, anc, O, scale=None, stream=None):
+    """medusa_tree_attn with the split-KV partials in the library's static
+    device scratch (no workspace; allocates nothing)."""
+    b, T, nq, d = Q.shape
+    nkv, Pmax = Kc.shape[1], Kc.shape[2]
+    _shape(Kc, (b, nkv, Pmax, d), "Kc")
+    _shape(Vc, (b, nkv, Pmax, d), "Vc")
+    _shape(seq_len, (b,), "seq_len")
+    _dt(seq_len, torch.int32, "seq_len")
+    _need(anc.dim() == 2 and anc.shape[0] == T, "anc: expected [T, words]")
+    _need(O.numel() == b * T * nq * d, "O: expected b*T*nq*d entries")
+    for t, n in ((Kc, "Kc"), (Vc, "Vc"), (O, "O")):
+        _dt(t, Q.dtype, n)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib().medusa_tree_attn_noalloc(_ptr(Q), _ptr(Kc), _ptr(Vc), _ptr(seq_len), _ptr(anc),
+                                        anc.shape[1], b, T, nq, nkv, d, Pmax, scale,
+                                        dtype_code(Q), _ptr(O), _stream(stream))
+    _check("medusa_tree_attn_noalloc", st)
 
 
 def _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus):

@@ -326,3 +326,22 @@ def test_split_heads_argument_checks():
     assert L.medusa_lm_logits(fake, 1, 128, fake, 10, 5, 0, fake, None) == ERR_ARG
     assert L.medusa_lm_logits(fake, 1, 128, fake, 10, M.BF16, 1, None, None) == ERR_ARG
     assert L.medusa_lm_logits(None, 0, 128, None, 10, M.BF16, 1, None, None) == 0
+
+
+def test_noalloc_attention_argument_checks():
+    """medusa_tree_attn_noalloc validates as medusa_tree_attn does; an empty
+    batch is a no-op; a shape whose split-KV partials exceed the static
+    scratch is refused before any device work."""
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 1, 1, 5, 6, 4, 128, 100, 0.1,
+                                      M.BF16, fake, None) == ERR_ARG
+    assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 1, 1, 5, 4, 4, 96, 100, 0.1,
+                                      M.BF16, fake, None) == ERR_UNSUPPORTED
+    assert L.medusa_tree_attn_noalloc(None, None, None, None, None, 2, 0, 65, 32, 32, 128, 2113,
+                                      0.1, M.BF16, None, None) == 0
+    big = M.medusa_tree_attn_workspace(2, 65, 32, 32, 128, 2113, M.BF16)
+    assert big > 16 << 20
+    assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 2, 2, 65, 32, 32, 128, 2113,
+                                      0.1, M.BF16, fake, None) == ERR_UNSUPPORTED
+    assert b"scratch" in L.medusa_last_error()
