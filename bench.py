@@ -2,13 +2,13 @@
 """Throughput of one Medusa draft-and-verify step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-heads + LM projection, shortlists, tree, tree attention, verify logits,
-acceptance, KV compaction (five library calls: shortlists + tree and acceptance
-+ compaction each run as one fused call, and the verify logits leave the
-acceptance statistics behind; see speculative_decoding_heads_amd/step.py).
-Default workload: the Llama-7B shape at batch 1 (hidden 4096, vocab 32000,
-4 heads, 64-candidate tree, 32 heads x 128, prefix 2048, bf16, greedy); the
-batch-16 typical-acceptance variant is measured too and reported alongside.
+the heads' residual blocks, their LM projection, shortlists + tree, tree
+attention, verify logits, acceptance + KV rollback (six library calls, the
+fused call sequence of speculative_decoding_heads_amd/step.py).  Default
+workload: the Llama-7B shape at batch 1 (hidden 4096, vocab 32000, 4 heads,
+64-candidate tree, 32 heads x 128, prefix 2048, bf16, greedy); the batch-16
+typical-acceptance variant ("also") and the 128k-vocabulary, 32k-context,
+batch-32 workload ("large") are measured too and reported alongside.
 
 Timing: inputs are resident in HBM; W warmup steps, then K timed steps between
 two events on the launch stream (synchronised on both sides).  Each step uses
@@ -16,7 +16,14 @@ its own seq_len buffer (preset to P), so no reset work runs inside the timed
 region.  When a workload's weights+cache are small enough to sit in the
 256 MB Infinity Cache across steps, two copies of every input are rotated.
 A second pass of K steps records events between the calls for the per-call
-breakdown and the roofline of the dominant kernel.
+times and the roofline of every call; the dominant call (most time among the
+calls that move algorithmic bytes) gives `roofline`.
+
+Algorithmic bytes and flops per call are those of the method (the head
+weights once, the LM projection once per pass, the prefix and tree K/V and the
+tree queries once); logits written by one call and read by the next are not
+counted, since they could be fused away.  The shortlist and acceptance calls
+move no algorithmic bytes beyond those and are bound by latency.
 
 With --loop S (default 8) the workload also runs as a steady-state loop: S
 consecutive steps with the state carried on the device, captured in one HIP
@@ -43,47 +50,67 @@ METRIC = "Medusa verify steps/sec at 7B shape (bs1, bs16) + % of HBM/MFMA roofli
 PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-CALLS = ["draft_heads", "topk_tree", "tree_attn", "verify_lm", "accept_compact"]
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)      # flop per byte
+CALLS = ["draft_hidden", "draft_lm", "topk_tree", "tree_attn", "verify_lm", "accept_compact"]
+# the kernel each single-GEMM call launches (for reading the counter summaries)
+KERNEL_OF = {"draft_hidden": "heads residual GEMM", "draft_lm": "heads LM GEMM",
+             "verify_lm": "verify LM GEMM", "tree_attn": "tree_attn_bf16 + attn_merge"}
 
 
 def alg_bytes(c):
-    """Algorithmic bytes each call must move (inputs read once, outputs written once)."""
+    """Algorithmic bytes each call must move (whole batch)."""
     e = 2 if c.dtype == "bf16" else 4
-    rows_d = c.b * (c.K + 1)
-    rows_v = c.b * c.T
     return {
-        "draft_heads": c.K * c.H * c.H * e + c.V * c.H * e + c.b * c.H * e
-        + 2 * rows_d * c.H * e + rows_d * c.V * 4,
-        "topk_tree": rows_d * c.V * 4 + c.b * c.T * 8,
-        "tree_attn": 2 * c.b * c.nkv * (c.P + c.T) * c.d * e + 2 * c.b * c.T * c.nq * c.d * e,
-        "verify_lm": c.V * c.H * e + rows_v * c.H * e + rows_v * c.V * 4,
-        "accept_compact": 4 * c.b * (c.K + 1) * c.nkv * c.d * e,
+        "draft_hidden": c.K * c.H * c.H * e,
+        "draft_lm": c.V * c.H * e,
+        "topk_tree": 0,
+        "tree_attn": 2 * c.b * c.nkv * (c.P + c.T) * c.d * e + c.b * c.T * c.nq * c.d * e,
+        "verify_lm": c.V * c.H * e,
+        "accept_compact": 0,
     }
 
 
 def alg_flops(c):
     return {
-        "draft_heads": 2 * c.b * c.K * c.H * c.H + 2 * c.b * (c.K + 1) * c.H * c.V,
+        "draft_hidden": 2 * c.b * c.K * c.H * c.H,
+        "draft_lm": 2 * c.b * (c.K + 1) * c.H * c.V,
+        "topk_tree": 0,
         "tree_attn": 4 * c.b * c.nq * c.T * (c.P + c.T) * c.d,
         "verify_lm": 2 * c.b * c.T * c.H * c.V,
+        "accept_compact": 0,
     }
 
 
 def _enqueue(st, x, step, M, c, ev=None):
-    """The five calls of VerifyStep.run (fused path), with optional events between them."""
+    """The six calls of VerifyStep.run (fused path), with optional events
+    ev[0..6] around them."""
     def mark(i):
         if ev is not None:
             ev[i].record()
     mark(0)
-    if st.draft == "hydra":            # the whole draft counts as draft_heads
+    if st.draft == "hydra":            # the whole draft counts as draft_hidden
         st.draft_hydra(x, step, st.root_mode, st.root)
         mark(1)
+        mark(2)
+        mark(3)
     else:
-        M.medusa_heads(x["h"], x["W"], x["LM"], st.logits, include_base=1, u_out=st.u)
+        M.medusa_heads_hidden(x["h"], x["W"], st.u, include_base=1)
         mark(1)
+        M.medusa_lm_logits(st.u, x["LM"], st.logits, reverse_k=1)
+        mark(2)
         _shortlists(st, x, step, M, c)
-    mark(2)
-    _verify(st, x, step, M, c, mark)
+        mark(3)
+    M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
+    mark(4)
+    M.medusa_verify_logits(st.O.view(c.b * c.T, c.nq * c.d), x["LM"],
+                           st.base_logits.view(c.b * c.T, c.V), st.mode, c.temperature,
+                           st.ws_verify)
+    mark(5)
+    M.medusa_accept_compact(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode,
+                            c.temperature, c.eps, c.delta, c.seed, step, st.L, st.path,
+                            st.acc_tokens, st.bonus, x["Kc"], x["Vc"], x["seq_len"], st.ws_acc,
+                            verify_ws=st.ws_verify)
+    mark(6)
 
 
 def _shortlists(st, x, step, M, c):
@@ -96,20 +123,6 @@ def _shortlists(st, x, step, M, c):
         M.medusa_topk_tree(st.logits, c.k, c.kmax, c.N, c.decay.numerator, c.decay.denominator,
                            st.root_mode, c.temperature, c.seed, step, x["seq_len"], st.root, st.idx,
                            st.val, st.tokens, st.pos, st.parent, st.depth, st.anc, st.ws_topk)
-
-
-def _verify(st, x, step, M, c, mark):
-    M.medusa_tree_attn(x["Q"], x["Kc"], x["Vc"], x["seq_len"], st.anc, st.O, ws=st.ws_attn)
-    mark(3)
-    M.medusa_verify_logits(st.O.view(c.b * c.T, c.nq * c.d), x["LM"],
-                           st.base_logits.view(c.b * c.T, c.V), st.mode, c.temperature,
-                           st.ws_verify)
-    mark(4)
-    M.medusa_accept_compact(st.base_logits, st.tokens, st.parent, st.depth, c.K, st.mode,
-                            c.temperature, c.eps, c.delta, c.seed, step, st.L, st.path,
-                            st.acc_tokens, st.bonus, x["Kc"], x["Vc"], x["seq_len"], st.ws_acc,
-                            verify_ws=st.ws_verify)
-    mark(5)
 
 
 def measure(cfg, steps, warmup, rotate=None, log=print, plan=None, draft="medusa"):
@@ -153,7 +166,8 @@ def measure(cfg, steps, warmup, rotate=None, log=print, plan=None, draft="medusa
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
 
-    # per-call pass
+    # per-call pass: events on the launch stream (torch's current stream, which
+    # every call above enqueues on) between the calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
            for _ in range(steps)]
     for j in range(steps):
@@ -163,7 +177,51 @@ def measure(cfg, steps, warmup, rotate=None, log=print, plan=None, draft="medusa
     per_call = {}
     for k, name in enumerate(CALLS):
         per_call[name] = 1000.0 * sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps   # us
+    del sets, seqs, st
+    torch.cuda.empty_cache()
     return ms, per_call
+
+
+def call_roofline(c, name, us):
+    """Roofline entry of one call: algorithmic bytes and flops per launch over
+    its event-timed average duration, against the bound its arithmetic
+    intensity selects (HBM below the ridge, bf16 MFMA above)."""
+    ab, af = alg_bytes(c)[name], alg_flops(c)[name]
+    t = us * 1e-6
+    if ab == 0 or t <= 0:
+        return {"bound": "latency", "avg_launch_us": round(us, 2)}
+    gbps = ab / t / 1e9
+    tflops = af / t / 1e12
+    out = {"avg_launch_us": round(us, 2), "alg_bytes_per_launch": ab, "alg_flops_per_launch": af,
+           "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "mfma_TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    if c.dtype == "bf16" and af / ab > RIDGE:
+        out.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": out["mfma_frac"]})
+    else:
+        out.update({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": out["hbm_frac"]})
+    return out
+
+
+def summarise(c, ms, per_call):
+    """value, per-call times, every call's roofline, the dominant call's roofline."""
+    rl = {k: call_roofline(c, k, per_call[k]) for k in CALLS}
+    moving = [k for k in CALLS if alg_bytes(c)[k] > 0]
+    dom = max(moving, key=lambda k: per_call[k])
+    roof = dict(rl[dom])
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(c.name, dom)
+    step_bytes = sum(alg_bytes(c).values())
+    step_flops = sum(alg_flops(c).values())
+    return {
+        "value": round(1000.0 / ms, 2), "ms_per_step": round(ms, 4),
+        "roofline": roof, "rooflines": rl,
+        "step_alg_bytes": step_bytes, "step_alg_flops": step_flops,
+        "step_effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+    }
 
 
 def measure_loop(cfg, steps_per_graph, replays, warmup_replays=2, log=print):
@@ -237,21 +295,37 @@ def tree_sweep(cfg, sizes, steps, warmup, log=print):
             "best_tokens_per_s": best["tokens_per_s"]}
 
 
-def cpu_baseline(cfg, seconds, log=print):
-    """The oracle (numpy float64) timed on this host on whole steps of the workload."""
-    import numpy as np
-    from oracle import oracle_step
-    from speculative_decoding_heads_amd.synth import make_inputs
+def host_identity():
+    """CPU model (from /proc/cpuinfo, as lscpu reports it), logical CPUs and
+    the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "cpus_allowed": allowed}
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        return (max([i.get("num_threads", 1) for i in info] or [1]),
+                sorted({i.get("internal_api", "?") for i in info}))
     except Exception:
-        cores = os.cpu_count()
-    c = cfg
-    host = make_inputs(c)
-    f = {k: v.float().numpy().astype(np.float64) for k, v in host.items()}
-    del host
-    P = np.full(c.b, c.P)
+        return None, []
+
+
+def _oracle_steps(c, f, P, seconds, log, tag):
+    from oracle import oracle_step
     done, t0 = 0, time.perf_counter()
     while True:
         oracle_step(f["h"], f["W"], f["LM"], f["Q"], f["Kc"], f["Vc"], P, c.k, c.N, c.decay,
@@ -259,12 +333,48 @@ def cpu_baseline(cfg, seconds, log=print):
                     delta=c.delta, seed=c.seed, step=done)
         done += 1
         el = time.perf_counter() - t0
-        log(f"[bench] oracle step {done}: {el:.1f}s")
+        log(f"[bench] oracle ({tag}) step {done}: {el:.1f}s")
         if el >= seconds or done >= 100:
-            break
-    return {"value": done / el, "unit": "verify-steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} full step(s) of the {c.name} workload, float64 numpy, "
-                      f"{el:.1f} s wall"}
+            return done, el
+
+
+def cpu_baseline(cfg, seconds, single_seconds, log=print):
+    """The oracle (numpy float64) timed on this host on whole steps of the
+    workload: once with numpy's BLAS threads as they come, once pinned to one
+    core (process affinity one CPU, BLAS limited to one thread)."""
+    import numpy as np
+    from speculative_decoding_heads_amd.synth import make_inputs
+    c = cfg
+    host = make_inputs(c)
+    f = {k: v.float().numpy().astype(np.float64) for k, v in host.items()}
+    del host
+    P = np.full(c.b, c.P)
+    threads, apis = _blas_threads()
+    done, el = _oracle_steps(c, f, P, seconds, log, f"{threads} BLAS threads")
+    out = {"value": done / el, "unit": "verify-steps/s", "cores": threads or os.cpu_count(),
+           "kind": "oracle",
+           "sample": f"{done} full step(s) of the {c.name} workload, float64 numpy, "
+                     f"{el:.1f} s wall, numpy BLAS with {threads} threads",
+           "host": host_identity(), "blas": apis}
+    if single_seconds > 0:
+        single = None
+        try:
+            from threadpoolctl import threadpool_limits
+            old = os.sched_getaffinity(0)
+            cpu = min(old)
+            os.sched_setaffinity(0, {cpu})
+            try:
+                with threadpool_limits(limits=1):
+                    d1, e1 = _oracle_steps(c, f, P, single_seconds, log, "one core")
+            finally:
+                os.sched_setaffinity(0, old)
+            single = {"value": d1 / e1, "unit": "verify-steps/s", "cores": 1,
+                      "sample": f"{d1} full step(s), process pinned to CPU {cpu}, "
+                                f"BLAS limited to one thread, {e1:.1f} s wall"}
+        except Exception as ex:            # affinity or threadpoolctl unavailable
+            single = {"error": str(ex)}
+        out["single_core"] = single
+    return out
 
 
 def kernel_source_hash(name):
@@ -274,15 +384,17 @@ def kernel_source_hash(name):
 
 
 def measured_traffic(workload, call):
-    """HBM bytes per launch of a call's kernel from the committed counter summary
-    (two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a copy of
-    known size), or None when absent or when the kernel source has changed."""
+    """HBM bytes per launch of a call's kernel(s) from the committed counter
+    summary (two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a
+    copy of known size), or None when absent or when a kernel source it names
+    has changed since."""
     path = os.path.join(PROFILES, f"traffic_{call}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_sha256") != kernel_source_hash(t["source"]):
+    srcs = t.get("sources") or {t["source"]: t["source_sha256"]}
+    if any(kernel_source_hash(s) != h for s, h in srcs.items()):
         return None
     return t["traffic_bytes_per_launch"]
 
@@ -326,6 +438,7 @@ def measured_peaks(log=print):
     a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     t_mm = timed(lambda: torch.matmul(a, b), 10)
+    del a, b
     out = {"copy_GBps": round(2 * n / t_copy / 1e9, 1), "read_GBps": round(n / t_read / 1e9, 1),
            "vendor_bf16_gemm_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
            "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_TFLOPs": BF16_PEAK_TFLOPS}
@@ -341,8 +454,12 @@ def main():
     ap.add_argument("--workload", default="llama7b_bs1")
     ap.add_argument("--also", default="llama7b_bs16",
                     help="second workload reported alongside ('' to skip)")
+    ap.add_argument("--large", default="vocab128k_ctx32k_bs32",
+                    help="large workload reported alongside, fewer steps ('' to skip)")
+    ap.add_argument("--large-steps", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-single-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--loop", type=int, default=8,
                     help="steps per captured graph for the steady-state loop (0 to skip)")
@@ -372,52 +489,35 @@ def main():
     log = lambda m: print(m, file=sys.stderr, flush=True)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
-    cfg = C.BY_NAME[args.workload]
-    if args.mode:
-        cfg = cfg.with_(mode=args.mode)
+
+    def cfg_of(name):
+        c = C.BY_NAME[name]
+        return c.with_(mode=args.mode) if args.mode else c
+
+    cfg = cfg_of(args.workload)
     ms, per_call = measure(cfg, args.steps, args.warmup, args.rotate, log)
-    value = 1000.0 / ms
-    ab, af = alg_bytes(cfg), alg_flops(cfg)
-    step_bytes = sum(ab.values())
-    dom = max(["verify_lm", "tree_attn"], key=lambda k: per_call[k])
-    t_dom = per_call[dom] * 1e-6
-    bytes_rate = ab[dom] / t_dom / 1e9
-    flop_rate = af.get(dom, 0) / t_dom / 1e12
-    ai = af.get(dom, 0) / ab[dom]
-    if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(flop_rate, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flop_rate / BF16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(bytes_rate, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(bytes_rate / HBM_PEAK_GBPS, 4)}
-    roof.update({"kernel": dom, "alg_bytes_per_launch": ab[dom],
-                 "alg_flops_per_launch": af.get(dom, 0), "avg_launch_us": round(per_call[dom], 2),
-                 "traffic": measured_traffic(cfg.name, dom)})
+    main_block = summarise(cfg, ms, per_call)
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "verify-steps/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "metric": METRIC, "value": main_block["value"], "unit": "verify-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_block["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.b, "hidden": cfg.H, "vocab": cfg.V,
                    "medusa_heads": cfg.K, "shortlist": list(cfg.k), "tree_candidates": cfg.N,
                    "q_heads": cfg.nq, "kv_heads": cfg.nkv, "head_dim": cfg.d, "prefix": cfg.P,
                    "acceptance": cfg.mode, "parallelism": "single-gpu"},
-        "roofline": roof,
-        "step_alg_bytes": step_bytes,
-        "step_effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
     }
-    if args.also:
-        c2 = C.BY_NAME[args.also]
-        if args.mode:
-            c2 = c2.with_(mode=args.mode)
-        ms2, pc2 = measure(c2, args.steps, args.warmup, None, log)
-        b2 = sum(alg_bytes(c2).values())
-        out["also"] = {"workload": c2.name, "value": round(1000.0 / ms2, 2),
-                       "unit": "verify-steps/s", "ms_per_step": round(ms2, 4),
-                       "step_effective_GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
-                       "per_call_us": {k: round(v, 2) for k, v in pc2.items()}}
+    out.update({k: v for k, v in main_block.items() if k not in ("value", "ms_per_step")})
+    for key, name, steps, warm in (("also", args.also, args.steps, args.warmup),
+                                   ("large", args.large, min(args.steps, args.large_steps),
+                                    min(args.warmup, 3))):
+        if not name:
+            continue
+        c2 = cfg_of(name)
+        ms2, pc2 = measure(c2, steps, warm, None, log)
+        blk = {"workload": c2.name, "unit": "verify-steps/s", "steps": steps, "warmup": warm}
+        blk.update(summarise(c2, ms2, pc2))
+        out[key] = blk
     if args.hydra:
         ms_h, pch = measure(cfg, args.steps, args.warmup, args.rotate, log, draft="hydra")
         out["hydra"] = {"workload": cfg.name, "draft": "hydra", "value": round(1000.0 / ms_h, 2),
@@ -434,7 +534,8 @@ def main():
         out["tree_sweep"] = tree_sweep(cfg, sizes, args.steps, args.warmup, log)
     torch.cuda.synchronize()
     out["measured_peaks"] = None if args.no_peaks else measured_peaks(log)
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds, log)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else \
+        cpu_baseline(cfg, args.cpu_seconds, args.cpu_single_seconds, log)
     print(json.dumps(out), flush=True)
 
 
