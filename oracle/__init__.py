@@ -22,7 +22,9 @@ Sources (web pages on Medusa heads; cited by page title and section):
     expected acceptance length as the throughput multiplier, the tree size as
     a tuned budget (module ``budget``).
   * zackli.ai, "Speculative Decoding Deep Dive II" ("Medusa"): Hydra-style
-    heads that see the token just drafted (module ``hydra``).
+    heads that see the token just drafted (module ``hydra``); ("MTP"):
+    heads that are transformer layers sharing one unembedding (module
+    ``mtp``).
 
 Every function states the passage it follows and, where the pages leave a step
 open, the reading taken.  Pins: ``tests/test_oracle_*.py``.
@@ -40,6 +42,7 @@ from .compact import kv_compact
 from .step import oracle_step
 from .budget import tree_plan_rates, expected_tokens, plan_from_tables, accept_tally
 from .hydra import hydra_draft
+from .mtp import mtp_draft, mtp_head, rmsnorm
 
 __all__ = [
     "round_bf16", "heads", "lm_project", "topk_stable", "argmax_lowest",
@@ -48,4 +51,5 @@ __all__ = [
     "path_attention", "accept_greedy_walk", "accept_greedy_parallel",
     "accept_typical", "typical_local", "accept_reject", "kv_compact", "oracle_step",
     "tree_plan_rates", "expected_tokens", "plan_from_tables", "accept_tally", "hydra_draft",
+    "mtp_draft", "mtp_head", "rmsnorm",
 ]
