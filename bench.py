@@ -52,9 +52,6 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)      # flop per byte
 CALLS = ["draft_hidden", "draft_lm", "topk_tree", "tree_attn", "verify_lm", "accept_compact"]
-# the kernel each single-GEMM call launches (for reading the counter summaries)
-KERNEL_OF = {"draft_hidden": "heads residual GEMM", "draft_lm": "heads LM GEMM",
-             "verify_lm": "verify LM GEMM", "tree_attn": "tree_attn_bf16 + attn_merge"}
 
 
 def alg_bytes(c):
@@ -88,8 +85,11 @@ def _enqueue(st, x, step, M, c, ev=None):
         if ev is not None:
             ev[i].record()
     mark(0)
-    if st.draft == "hydra":            # the whole draft counts as draft_hidden
-        st.draft_hydra(x, step, st.root_mode, st.root)
+    if st.draft in ("hydra", "mtp"):   # the whole draft counts as draft_hidden
+        if st.draft == "hydra":
+            st.draft_hydra(x, step, st.root_mode, st.root)
+        else:
+            st.draft_mtp(x, step, st.root_mode, st.root)
         mark(1)
         mark(2)
         mark(3)
@@ -129,21 +129,24 @@ def measure(cfg, steps, warmup, rotate=None, log=print, plan=None, draft="medusa
     import torch
     from speculative_decoding_heads_amd import medusa as M
     from speculative_decoding_heads_amd.step import VerifyStep, device_inputs
-    from speculative_decoding_heads_amd.synth import make_inputs
+    from speculative_decoding_heads_amd.synth import make_inputs, make_mtp_inputs
 
     M.lib()
     c = cfg
     t0 = time.time()
     names = ("h", "W", "LM", "Kc", "Vc", "Q") + (("E",) if draft == "hydra" else ())
     host = make_inputs(c, names)
-    ws_bytes = sum(v.numel() * v.element_size() for v in host.values())
+    mtp = make_mtp_inputs(c) if draft == "mtp" else {}
+    ws_bytes = sum(v.numel() * v.element_size() for v in list(host.values()) + list(mtp.values()))
     if rotate is None:
         rotate = 2 if ws_bytes < (1 << 30) else 1
     sets = []
     for r in range(rotate):
         x = device_inputs(c, host)
+        if mtp:
+            x["mtp"] = {n: t.to("cuda") for n, t in mtp.items()}
         sets.append(x)
-    del host
+    del host, mtp
     log(f"[bench] {c.name}: inputs {ws_bytes / 1e6:.1f} MB x {rotate} copies "
         f"({time.time() - t0:.1f}s)")
     st = VerifyStep(c, plan=plan, draft=draft)
@@ -473,6 +476,9 @@ def main():
     ap.add_argument("--hydra", action="store_true",
                     help="also time the step with the Hydra-style draft (medusa_hydra_draft: "
                          "one LM pass per tree depth) on the same workload")
+    ap.add_argument("--mtp", action="store_true",
+                    help="also time the step with MTP-style draft heads (medusa_mtp_draft: one "
+                         "transformer layer of the Llama layer shape per head) on the same workload")
     ap.add_argument("--tree-sweep", default="",
                     help="comma-separated candidate counts: measure the tree budget "
                          "(expected tokens per second per tree size) on the workload")
@@ -523,6 +529,20 @@ def main():
         out["hydra"] = {"workload": cfg.name, "draft": "hydra", "value": round(1000.0 / ms_h, 2),
                         "unit": "verify-steps/s", "ms_per_step": round(ms_h, 4),
                         "per_call_us": {k: round(v, 2) for k, v in pch.items()}}
+    if args.mtp:
+        from speculative_decoding_heads_amd.synth import mtp_width
+        ms_m, pcm = measure(cfg, args.steps, args.warmup, args.rotate, log, draft="mtp")
+        F = mtp_width(cfg.H)
+        e = 2
+        layer = (cfg.nq + 2 * cfg.nkv) * cfg.d * cfg.H + cfg.H * cfg.nq * cfg.d + 3 * F * cfg.H
+        draft_bytes = cfg.K * layer * e + cfg.V * cfg.H * e \
+            + cfg.K * 2 * cfg.b * cfg.nkv * cfg.P * cfg.d * e
+        t = pcm["draft_hidden"] * 1e-6
+        out["mtp"] = {"workload": cfg.name, "draft": "mtp", "value": round(1000.0 / ms_m, 2),
+                      "unit": "verify-steps/s", "ms_per_step": round(ms_m, 4),
+                      "mlp_width": F, "draft_alg_bytes": draft_bytes,
+                      "draft_hbm_frac": round(draft_bytes / t / 1e9 / HBM_PEAK_GBPS, 4),
+                      "per_call_us": {k: round(v, 2) for k, v in pcm.items()}}
     if args.loop > 0:
         ms_l = measure_loop(cfg, args.loop, args.loop_replays, log=log)
         out["loop"] = {"workload": cfg.name, "value": round(1000.0 / ms_l, 2),

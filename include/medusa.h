@@ -478,6 +478,47 @@ int medusa_hydra_draft(const void* h, int32_t b, int32_t H, const void* E, int32
                        int32_t anc_words, float* logits_out, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * medusa_mtp_draft - MTP-style draft heads: one transformer layer per head.
+ * zackli.ai "Speculative Decoding Deep Dive II: Medusa, MTP", "MTP": the
+ * trunk's h_t feeds n heads that are transformer layers f_{h_i}, the logits
+ * are f_u(f_{h_i}(h_t)) through one shared unembedding, and the drafts take
+ * the same tree verification as Medusa heads.  Reading taken (the page gives
+ * no layer shape): head i is one pre-norm layer of the trunk's kind at the
+ * current position,
+ *   a  = RMSNorm(h; g1_i)                 RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g
+ *   q, k, v = a Wq_i^T, a Wk_i^T, a Wv_i^T      (nq / nkv heads of dim d)
+ *   o  = softmax(q k^T / sqrt(d)) v  over the head's cache [0, P) and (k, v)
+ *        at slot P = seq_len[s]; q head j reads kv head floor(j * nkv / nq)
+ *   x1 = h + o Wo_i^T,  a2 = RMSNorm(x1; g2_i)
+ *   y  = x1 + (SiLU(a2 Wg_i^T) * (a2 Wu_i^T)) Wd_i^T
+ * and the outputs are those of medusa_heads: u [b, K+1, H] (slot 0 = h, slot
+ * i = y of head i) and logits [b, K+1, V] f32 = LM u, so medusa_topk_tree and
+ * the rest of the step follow unchanged.
+ *
+ *   h [b, H]; g1, g2 [K, H]; Wqkv [K, (nq + 2 nkv) d, H] (rows: Wq, then Wk,
+ *   then Wv); Wo [K, H, nq d]; Wgu [K, 2F, H] with rows 2j = Wg row j and
+ *   2j+1 = Wu row j (interleaved); Wd [K, H, F]; LM [V, H]: bf16, device.
+ *   Kh, Vh [K, b, nkv, Pmax, d] bf16: each head's cache; on return slot
+ *   seq_len[s] of every head holds the current position's k, v (nothing is
+ *   written for a sequence with seq_len outside [0, Pmax), whose attention
+ *   rows are then NaN).  seq_len [b] device, not changed.
+ *   u_out [b, K+1, H] bf16 or NULL (kept in the workspace); logits f32.
+ *   ws: medusa_mtp_workspace(b, H, K, F, nq, nkv, d, Pmax, u_out != NULL)
+ *   bytes, 16-byte aligned.
+ * Requires H, F and nq*d multiples of 128, d in {64, 128}, nq % nkv == 0,
+ * every pointer 16-byte aligned.  bf16 operands with f32 accumulation;
+ * a, q, k, v, o, x1, a2, the SwiGLU product and y are stored in bf16.
+ * ------------------------------------------------------------------------- */
+size_t medusa_mtp_workspace(int32_t b, int32_t H, int32_t K, int32_t F, int32_t nq, int32_t nkv,
+                            int32_t d, int32_t Pmax, int32_t keep_u);
+int medusa_mtp_draft(const void* h, int32_t b, int32_t H, int32_t K, const void* g1,
+                     const void* Wqkv, const void* Wo, const void* g2, const void* Wgu,
+                     const void* Wd, int32_t F, float eps, void* Kh, void* Vh,
+                     const int32_t* seq_len, int32_t nq, int32_t nkv, int32_t d, int32_t Pmax,
+                     const void* LM, int32_t V, void* u_out, float* logits, void* ws,
+                     size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

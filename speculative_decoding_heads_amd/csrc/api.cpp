@@ -153,6 +153,51 @@ int medusa_lm_logits(const void* x, int64_t rows, int32_t H, const void* LM, int
                     "LM projection");
 }
 
+// ------------------------------------------------------------------- MTP-style heads
+static int mtp_check(int32_t b, int32_t H, int32_t K, int32_t F, int32_t nq, int32_t nkv, int32_t d,
+              int32_t Pmax, int32_t V) {
+  if (b < 0) return fail(MEDUSA_ERR_ARG, "b < 0");
+  if (K < 1 || K > MEDUSA_MAX_HEADS) return fail(MEDUSA_ERR_ARG, "K out of range [1, 16]");
+  if (H <= 0 || F <= 0 || V <= 0) return fail(MEDUSA_ERR_ARG, "H, F and V must be positive");
+  if (nq < 1 || nkv < 1 || nq % nkv != 0) return fail(MEDUSA_ERR_ARG, "need nq % nkv == 0");
+  if (d != 64 && d != 128) return fail(MEDUSA_ERR_UNSUPPORTED, "MTP attention supports d = 64 or 128");
+  if (H % 128 != 0 || F % 128 != 0 || (nq * d) % 128 != 0)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "MTP heads need H, F and nq * d multiples of 128");
+  if (Pmax < 1) return fail(MEDUSA_ERR_ARG, "Pmax must be positive");
+  if ((int64_t)b * K > INT32_MAX / 4 || (int64_t)b * (K + 1) > INT32_MAX / 4)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "too many rows");
+  if ((int64_t)(nq + 2 * nkv) * d > INT32_MAX / 4 || (int64_t)2 * F > INT32_MAX / 4)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "layer too wide");
+  return MEDUSA_OK;
+}
+
+size_t medusa_mtp_workspace(int32_t b, int32_t H, int32_t K, int32_t F, int32_t nq, int32_t nkv,
+                            int32_t d, int32_t Pmax, int32_t keep_u) {
+  if (b <= 0 || K < 1 || H <= 0 || F <= 0 || nq < 1 || nkv < 1 || nq % nkv || Pmax < 1) return 0;
+  if (d != 64 && d != 128) return 0;
+  return round_up(mtp_layout(b, H, K, F, nq, nkv, d, Pmax, keep_u == 0).bytes);
+}
+
+int medusa_mtp_draft(const void* h, int32_t b, int32_t H, int32_t K, const void* g1,
+                     const void* Wqkv, const void* Wo, const void* g2, const void* Wgu,
+                     const void* Wd, int32_t F, float eps, void* Kh, void* Vh,
+                     const int32_t* seq_len, int32_t nq, int32_t nkv, int32_t d, int32_t Pmax,
+                     const void* LM, int32_t V, void* u_out, float* logits, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (int s = mtp_check(b, H, K, F, nq, nkv, d, Pmax, V)) return s;
+  if (!(eps >= 0.f && std::isfinite(eps))) return fail(MEDUSA_ERR_ARG, "eps must be finite and >= 0");
+  if (b == 0) return MEDUSA_OK;
+  if (!h || !g1 || !Wqkv || !Wo || !g2 || !Wgu || !Wd || !Kh || !Vh || !seq_len || !LM || !logits)
+    return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  const void* al[] = {h, g1, Wqkv, Wo, g2, Wgu, Wd, Kh, Vh, LM, u_out, ws};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(MEDUSA_ERR_ARG, "MTP operands must be 16-byte aligned");
+  const size_t need = medusa_mtp_workspace(b, H, K, F, nq, nkv, d, Pmax, u_out != nullptr);
+  if (!ws || ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "mtp_draft: workspace too small");
+  MtpArgs a{h, b, H, K, F, g1, Wqkv, Wo, g2, Wgu, Wd, eps, Kh, Vh, seq_len, nq, nkv, d, Pmax, LM, V};
+  return hip_status(run_mtp_draft(a, u_out, logits, ws, as_stream(stream)), "mtp_draft");
+}
+
 // ------------------------------------------------------------------- verify logits + partials
 size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode) {
   if (rows <= 0 || H <= 0 || V <= 0 || !dtype_ok(dtype)) return 0;

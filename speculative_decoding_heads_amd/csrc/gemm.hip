@@ -142,13 +142,88 @@ struct EpiHeads {
   }
 };
 
+// ---------------------------------------------------------------- MTP layer epilogues
+// One transformer layer per MTP head, its GEMMs batched over the heads
+// (blockIdx.y = head).  Columns arrive four at a time (n % 4 == 0, N % 4 == 0).
+// q | k | v of the current position: q -> Q [heads, M, nqd]; k, v -> the
+// head's cache [heads, M, nkv, Pmax, d] at slot seq_len[m] (nothing is
+// written for a sequence whose slot lies outside the cache).
+struct EpiQKV {
+  uint16_t* Q;
+  uint16_t* Kc;
+  uint16_t* Vc;
+  const int* seq_len;
+  int nqd, nkvd, d, Pmax, M, N;
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M || n >= N) return;
+    const int hd = blockIdx.y;
+    uint2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    if (n < nqd) {
+      *reinterpret_cast<uint2*>(Q + ((int64_t)hd * M + m) * nqd + n) = w;
+      return;
+    }
+    int c = n - nqd;
+    uint16_t* C = Kc;
+    if (c >= nkvd) {
+      c -= nkvd;
+      C = Vc;
+    }
+    const int P = seq_len[m];
+    if (P < 0 || P >= Pmax) return;
+    const int g = c / d, e = c - g * d;
+    const int nkv = nkvd / d;
+    *reinterpret_cast<uint2*>(C + ((((int64_t)hd * M + m) * nkv + g) * Pmax + P) * d + e) = w;
+  }
+  __device__ __forceinline__ void copy_base(int, int) const {}
+};
+// out = bf16(R + z): O at O + head * so + m * ldo + n, R likewise (sr = 0: one
+// residual for every head).
+struct EpiResid {
+  uint16_t* O;
+  const uint16_t* R;
+  int64_t so, ldo, sr, ldr;
+  int M, N;
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M || n >= N) return;
+    const int hd = blockIdx.y;
+    const uint2 r = *reinterpret_cast<const uint2*>(R + hd * sr + (int64_t)m * ldr + n);
+    uint2 w;
+    w.x = pack_bf16x2(bf16_lo(r.x) + v[0], bf16_hi(r.x) + v[1]);
+    w.y = pack_bf16x2(bf16_lo(r.y) + v[2], bf16_hi(r.y) + v[3]);
+    *reinterpret_cast<uint2*>(O + hd * so + (int64_t)m * ldo + n) = w;
+  }
+  __device__ __forceinline__ void copy_base(int, int) const {}
+};
+// SwiGLU on weight rows interleaved (gate_j, up_j) = rows (2j, 2j + 1):
+// out[j] = bf16(SiLU(gate_j) * up_j) at O + head * so + m * ldo.
+struct EpiSwiGLU {
+  uint16_t* O;
+  int64_t so, ldo;
+  int M, N;
+  __device__ __forceinline__ void store4(int m, int n, f32x4 v) const {
+    if (m >= M || n >= N) return;
+    const int hd = blockIdx.y;
+    const float a = v[0] / (1.0f + expf(-v[0])) * v[1];
+    const float b = v[2] / (1.0f + expf(-v[2])) * v[3];
+    *reinterpret_cast<uint32_t*>(O + hd * so + (int64_t)m * ldo + (n >> 1)) = pack_bf16x2(a, b);
+  }
+  __device__ __forceinline__ void copy_base(int, int) const {}
+};
+
 // ---------------------------------------------------------------- skinny bf16
 // grid.x = ceil(N / (16*NB)); block = 256 (4 waves splitting K in 128-chunks).
+// grid.y = independent problems of the same shape (X, W advanced by bsx, bsw
+// elements per problem; the epilogue reads blockIdx.y for its outputs).
 template <int NB, int MB, class Epi>
 __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restrict__ X,
                                                         int64_t ldx, int M,
                                                         const uint16_t* __restrict__ W,
-                                                        int N, int Kd, Epi epi) {
+                                                        int N, int Kd, Epi epi, int64_t bsx,
+                                                        int64_t bsw) {
+  X += blockIdx.y * bsx;
+  W += blockIdx.y * bsw;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int n0 = blockIdx.x * 16 * NB;
@@ -259,7 +334,10 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
                                                                int64_t ldx, int M,
                                                                const uint16_t* __restrict__ W,
                                                                int N, int Kd, int ntm, Epi epi,
-                                                               bool rev) {
+                                                               bool rev, int64_t bsx,
+                                                               int64_t bsw) {
+  X += blockIdx.y * bsx;                       // grid.y: independent problems, as skinny
+  W += blockIdx.y * bsw;
   constexpr int NT = 64 * NWAVES;
   constexpr int BM = 16 * MB;
   constexpr int BN = 16 * NBW * NWAVES;
@@ -659,21 +737,22 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
 
 template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
-                              int Kd, const Epi& epi, hipStream_t st, bool rev = false) {
+                              int Kd, const Epi& epi, hipStream_t st, bool rev = false,
+                              int batch = 1, int64_t bsx = 0, int64_t bsw = 0) {
   // logits always take the tiled / ring kernels, so the verify-rows logits of
   // medusa_heads and medusa_verify_logits come from the same kernel
   const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
   if (p.kind == 0) {
     // skinny: 4 waves split K, X (a few rows) read from L2
     if (p.snb == 2)
-      hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
-                         M, W, N, Kd, epi);
+      hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
+                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
     else if (p.mb == 1)
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 1, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
-                         M, W, N, Kd, epi);
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
+                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
     else
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 2, Epi>), dim3(p.ntiles), dim3(256), 0, st, X, ldx,
-                         M, W, N, Kd, epi);
+      hipLaunchKernelGGL((gemm_skinny_bf16<1, 2, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
+                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
     return hipGetLastError();
   }
   if constexpr (IsLogits<Epi>::value) if (p.kind == 2) {
@@ -701,8 +780,8 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
 #define TILED_NW(MB_, NW_)                                                                     \
   do {                                                                                         \
     const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
-    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * p.ntiles), dim3(64 * NW_), \
-                       0, st, X, ldx, M, W, N, Kd, ntm, epi, rev);                             \
+    hipLaunchKernelGGL((gemm_tiled_bf16<MB_, 1, Epi, NW_>), dim3(ntm * p.ntiles, batch),      \
+                       dim3(64 * NW_), 0, st, X, ldx, M, W, N, Kd, ntm, epi, rev, bsx, bsw);   \
   } while (0)
 #define TILED(MB_)                                                                             \
   do {                                                                                         \
@@ -771,6 +850,29 @@ hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int
                        H, epi, st, rev);
   return launch_f32(static_cast<const float*>(x), H, M, static_cast<const float*>(LM), V, H, epi,
                     st);
+}
+
+// ---------------------------------------------------------------- MTP layer GEMMs
+hipError_t run_mtp_qkv(const uint16_t* a, int M, int H, const uint16_t* Wqkv, int heads, int nq,
+                       int nkv, int d, uint16_t* Q, uint16_t* Kc, uint16_t* Vc,
+                       const int* seq_len, int Pmax, hipStream_t st) {
+  const int N = (nq + 2 * nkv) * d;
+  EpiQKV epi{Q, Kc, Vc, seq_len, nq * d, nkv * d, d, Pmax, M, N};
+  return launch_bf16(a, H, M, Wqkv, N, H, epi, st, false, heads, (int64_t)M * H, (int64_t)N * H);
+}
+
+hipError_t run_mtp_resid(const uint16_t* x, int64_t ldx, int64_t sx, int M, int Kd,
+                         const uint16_t* W, int N, int heads, uint16_t* O, int64_t so,
+                         int64_t ldo, const uint16_t* R, int64_t sr, int64_t ldr, hipStream_t st) {
+  EpiResid epi{O, R, so, ldo, sr, ldr, M, N};
+  return launch_bf16(x, ldx, M, W, N, Kd, epi, st, false, heads, sx, (int64_t)N * Kd);
+}
+
+hipError_t run_mtp_swiglu(const uint16_t* a, int M, int H, const uint16_t* Wgu, int F, int heads,
+                          uint16_t* z, hipStream_t st) {
+  EpiSwiGLU epi{z, (int64_t)M * F, (int64_t)F, M, 2 * F};
+  return launch_bf16(a, H, M, Wgu, 2 * F, H, epi, st, false, heads, (int64_t)M * H,
+                     (int64_t)2 * F * H);
 }
 
 // ---------------------------------------------------------------- verify logits + partials

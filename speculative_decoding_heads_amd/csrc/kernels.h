@@ -39,6 +39,28 @@ size_t verify_workspace(int M, int N, int Kd, int dtype, int mode);
 hipError_t run_verify_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
                              float* logits, int mode, float temperature, void* ws, hipStream_t st);
 
+// ---- MTP-style heads: one transformer layer per head, batched over heads
+// (gemm.hip: the layer's GEMMs; mtp.hip: RMSNorm and the draft driver)
+hipError_t run_mtp_qkv(const uint16_t* a, int M, int H, const uint16_t* Wqkv, int heads, int nq,
+                       int nkv, int d, uint16_t* Q, uint16_t* Kc, uint16_t* Vc,
+                       const int* seq_len, int Pmax, hipStream_t st);
+hipError_t run_mtp_resid(const uint16_t* x, int64_t ldx, int64_t sx, int M, int Kd,
+                         const uint16_t* W, int N, int heads, uint16_t* O, int64_t so,
+                         int64_t ldo, const uint16_t* R, int64_t sr, int64_t ldr, hipStream_t st);
+hipError_t run_mtp_swiglu(const uint16_t* a, int M, int H, const uint16_t* Wgu, int F, int heads,
+                          uint16_t* z, hipStream_t st);
+struct MtpArgs {
+  const void* h;                       // [b, H]
+  int b, H, K, F;
+  const void *g1, *Wqkv, *Wo, *g2, *Wgu, *Wd;
+  float eps;
+  void *Kh, *Vh;                       // [K, b, nkv, Pmax, d]
+  const int* seq_len;                  // [b]
+  int nq, nkv, d, Pmax;
+  const void* LM;
+  int V;
+};
+
 // ---- top-k shortlists and root (topk.hip)
 struct TopkArgs {
   int b, K, V, kmax;
@@ -113,6 +135,13 @@ struct AttnPlan {
   int tiles_per_split;  // 64-key tiles per partition
 };
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
+// MTP draft workspace regions (byte offsets) and the attention plan it uses
+struct MtpLayout {
+  size_t a, a2, x1, q, o, z, u, seq, anc, attn, bytes;
+  AttnPlan plan;
+};
+MtpLayout mtp_layout(int M, int H, int K, int F, int nq, int nkv, int d, int Pmax, bool own_u);
+hipError_t run_mtp_draft(const MtpArgs& a, void* u_out, float* logits, void* ws, hipStream_t st);
 // the static scratch of the no-allocation attention call: its size, and its
 // device address on the current device (looked up once per device)
 constexpr size_t kAttnScratchBytes = size_t(16) << 20;

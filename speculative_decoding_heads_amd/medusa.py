@@ -58,6 +58,9 @@ _SIGS = {
                           _P, _P, _SZ, _P], _I32),
     "medusa_tree_attn_noalloc": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                   _F, _I32, _P, _P], _I32),
+    "medusa_mtp_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "medusa_mtp_draft": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _P, _I32,
+                          _I32, _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
     "medusa_accept_workspace": ([_I32, _I32], _SZ),
     "medusa_accept": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _F, _F, _U64, _U64, _P, _P,
                        _P, _P, _P, _SZ, _P], _I32),
@@ -366,6 +369,48 @@ def medusa_tree_attn_noalloc(Q, Kc, Vc, seq_len, anc, O, scale=None, stream=None
                                         anc.shape[1], b, T, nq, nkv, d, Pmax, scale,
                                         dtype_code(Q), _ptr(O), _stream(stream))
     _check("medusa_tree_attn_noalloc", st)
+
+
+def medusa_mtp_workspace(b, H, K, F, nq, nkv, d, Pmax, keep_u=True):
+    return lib().medusa_mtp_workspace(b, H, K, F, nq, nkv, d, Pmax, 1 if keep_u else 0)
+
+
+def medusa_mtp_draft(h, w, LM, Kh, Vh, seq_len, logits, u_out=None, eps=1e-6, ws=None,
+                     stream=None):
+    """MTP-style draft heads.  w: dict of bf16 device tensors g1 [K, H],
+    Wqkv [K, (nq + 2 nkv) d, H], Wo [K, H, nq d], g2 [K, H], Wgu [K, 2F, H]
+    (gate / up rows interleaved), Wd [K, H, F]; Kh, Vh [K, b, nkv, Pmax, d]."""
+    b, H = h.shape
+    K, _, nkv, Pmax, d = Kh.shape
+    F = w["Wd"].shape[2]
+    nq = w["Wo"].shape[2] // d
+    V = LM.shape[0]
+    _shape(w["g1"], (K, H), "g1")
+    _shape(w["g2"], (K, H), "g2")
+    _shape(w["Wqkv"], (K, (nq + 2 * nkv) * d, H), "Wqkv")
+    _shape(w["Wo"], (K, H, nq * d), "Wo")
+    _shape(w["Wgu"], (K, 2 * F, H), "Wgu")
+    _shape(w["Wd"], (K, H, F), "Wd")
+    _shape(Vh, (K, b, nkv, Pmax, d), "Vh")
+    _shape(LM, (V, H), "LM")
+    _shape(seq_len, (b,), "seq_len")
+    _dt(seq_len, torch.int32, "seq_len")
+    for t, n in [(h, "h"), (LM, "LM"), (Kh, "Kh"), (Vh, "Vh")] + [(w[k], k) for k in
+                                                                  ("g1", "Wqkv", "Wo", "g2", "Wgu",
+                                                                   "Wd")]:
+        _dt(t, torch.bfloat16, n)
+    _need(logits.numel() == b * (K + 1) * V and logits.shape[-1] == V,
+          "logits: expected b*(K+1)*V entries")
+    _dt(logits, torch.float32, "logits")
+    if u_out is not None:
+        _need(u_out.numel() == b * (K + 1) * H, "u_out: expected b*(K+1)*H entries")
+        _dt(u_out, torch.bfloat16, "u_out")
+    st = lib().medusa_mtp_draft(_ptr(h), b, H, K, _ptr(w["g1"]), _ptr(w["Wqkv"]), _ptr(w["Wo"]),
+                                _ptr(w["g2"]), _ptr(w["Wgu"]), _ptr(w["Wd"]), F, eps, _ptr(Kh),
+                                _ptr(Vh), _ptr(seq_len), nq, nkv, d, Pmax, _ptr(LM), V,
+                                _ptr(u_out), _ptr(logits), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream))
+    _check("medusa_mtp_draft", st)
 
 
 def _accept_shapes(base_logits, tokens, parent, depth, K, L, path, acc_tokens, bonus):

@@ -34,8 +34,8 @@ class VerifyStep:
         "hydra" (medusa_hydra_draft: head d on h + E[previous token], one LM
         pass per depth; bf16 and the fused path only; x needs "E")."""
         self.cfg = c = cfg
-        if draft not in ("medusa", "hydra"):
-            raise ValueError("draft must be 'medusa' or 'hydra'")
+        if draft not in ("medusa", "hydra", "mtp"):
+            raise ValueError("draft must be 'medusa', 'hydra' or 'mtp'")
         self.draft = draft
         if plan is not None:
             parent, rank = list(plan[0]), list(plan[1])
@@ -85,6 +85,10 @@ class VerifyStep:
                 self.plan = (list(par), list(rk))
             self.ws_hydra = M.workspace(
                 M.medusa_hydra_workspace(c.b, c.H, c.V, c.k, c.kmax, *self.plan), device)
+        if draft == "mtp":
+            if dt != M.BF16:
+                raise ValueError("the MTP draft runs in bf16")
+            self.ws_mtp = None          # sized on first use (the layer width comes with x)
 
     def run(self, x, step=0, stream=None, fused=True, root_given=False):
         """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len.
@@ -97,6 +101,10 @@ class VerifyStep:
             if not fused:
                 raise ValueError("the Hydra draft needs the fused path")
             self.draft_hydra(x, step, root_mode, root, stream)
+        elif self.draft == "mtp":
+            if not fused:
+                raise ValueError("the MTP draft needs the fused path")
+            self.draft_mtp(x, step, root_mode, root, stream)
         else:
             self.draft_medusa(x, step, root_mode, root, fused, stream)
         self.verify(x, step, fused, stream)
@@ -130,6 +138,24 @@ class VerifyStep:
             M.medusa_build_tree(c.k, self.N, c.decay.numerator, c.decay.denominator, self.root,
                                 self.idx, x["seq_len"], self.tokens, self.pos, self.parent,
                                 self.depth, self.anc, stream=stream)
+
+    def draft_mtp(self, x, step, root_mode, root, stream=None):
+        """The MTP-style draft of one step: K transformer-layer heads on h
+        (medusa_mtp_draft: head logits in the layout of medusa_heads), then
+        shortlists and tree as for Medusa heads.  x needs "mtp": the layers'
+        weights and caches (synth.make_mtp_inputs, on the device)."""
+        c = self.cfg
+        w = x["mtp"]
+        if self.ws_mtp is None:
+            F = w["Wd"].shape[2]
+            self.ws_mtp = M.workspace(M.medusa_mtp_workspace(c.b, c.H, c.K, F, c.nq, c.nkv, c.d,
+                                                             w["Kh"].shape[3]), self.device)
+        M.medusa_mtp_draft(x["h"], w, x["LM"], w["Kh"], w["Vh"], x["seq_len"], self.logits,
+                           u_out=self.u, ws=self.ws_mtp, stream=stream)
+        M.medusa_topk_tree(self.logits, c.k, c.kmax, self.N, c.decay.numerator,
+                           c.decay.denominator, root_mode, c.temperature, c.seed, step,
+                           x["seq_len"], root, self.idx, self.val, self.tokens, self.pos,
+                           self.parent, self.depth, self.anc, self.ws_topk, stream=stream)
 
     def draft_hydra(self, x, step, root_mode, root, stream=None):
         """The Hydra-style draft of one step: root, tree tables and tokens."""

@@ -16,7 +16,8 @@ stays bounded.
 
 import torch
 
-TENSOR_IDS = {"h": 0, "W": 1, "LM": 2, "Kc": 3, "Vc": 4, "Q": 5, "E": 6}
+TENSOR_IDS = {"h": 0, "W": 1, "LM": 2, "Kc": 3, "Vc": 4, "Q": 5, "E": 6,
+              "g1": 7, "Wqkv": 8, "Wo": 9, "g2": 10, "Wgu": 11, "Wd": 12, "Kh": 13, "Vh": 14}
 WEIGHT_STD = 0.02
 
 
@@ -71,4 +72,33 @@ def make_inputs(cfg, names=("h", "W", "LM", "Kc", "Vc", "Q")):
     for n in names:
         std = WEIGHT_STD if n in ("W", "LM") else 1.0
         out[n] = _chunked(shapes[n], cfg.index, n, std, cfg.dtype)
+    return out
+
+
+def mtp_width(H):
+    """SwiGLU width of an MTP head layer: 8H/3 rounded up to a multiple of 256
+    (11008 at H = 4096, the Llama-7B layer)."""
+    return ((8 * H + 2) // 3 + 255) // 256 * 256
+
+
+def make_mtp_inputs(cfg, F=None):
+    """Host tensors of K MTP-style head layers for a workload (bf16):
+    g1, g2 [K, H] = 1 + 0.02 N(0, 1); Wqkv [K, (nq + 2 nkv) d, H], Wo [K, H, nq d],
+    Wgu [K, 2F, H] (gate / up rows interleaved), Wd [K, H, F] ~ N(0, 0.02^2);
+    the heads' caches Kh, Vh [K, b, nkv, Pmax, d] ~ N(0, 1)."""
+    c = cfg
+    F = F or mtp_width(c.H)
+    K = c.K
+    shapes = {
+        "Wqkv": (K, (c.nq + 2 * c.nkv) * c.d, c.H), "Wo": (K, c.H, c.nq * c.d),
+        "Wgu": (K, 2 * F, c.H), "Wd": (K, c.H, F),
+        "Kh": (K, c.b, c.nkv, c.Pmax, c.d), "Vh": (K, c.b, c.nkv, c.Pmax, c.d),
+    }
+    out = {}
+    for n in ("g1", "g2"):
+        g = normal((K, c.H), seed_of(c.index, TENSOR_IDS[n]), WEIGHT_STD, "f32") + 1.0
+        out[n] = g.to(torch.bfloat16)
+    for n, shp in shapes.items():
+        std = 1.0 if n in ("Kh", "Vh") else WEIGHT_STD
+        out[n] = _chunked(shp, c.index, n, std, "bf16")
     return out

@@ -345,3 +345,25 @@ def test_noalloc_attention_argument_checks():
     assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 2, 2, 65, 32, 32, 128, 2113,
                                       0.1, M.BF16, fake, None) == ERR_UNSUPPORTED
     assert b"scratch" in L.medusa_last_error()
+
+
+def test_mtp_draft_argument_checks():
+    """medusa_mtp_draft validates shapes, alignment and workspace before any
+    launch; an empty batch is a no-op."""
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)
+    args = lambda b=1, H=256, K=2, F=256, nq=2, nkv=2, d=128, Pmax=10, V=100, ws_bytes=1 << 26, \
+        h=fake, eps=1e-6: (h, b, H, K, fake, fake, fake, fake, fake, fake, F, eps, fake, fake,
+                           fake, nq, nkv, d, Pmax, fake, V, fake, fake, fake, ws_bytes, None)
+    assert L.medusa_mtp_draft(*args(K=0)) == ERR_ARG
+    assert L.medusa_mtp_draft(*args(nq=3, nkv=2)) == ERR_ARG
+    assert L.medusa_mtp_draft(*args(d=96)) == ERR_UNSUPPORTED
+    assert L.medusa_mtp_draft(*args(H=200)) == ERR_UNSUPPORTED
+    assert L.medusa_mtp_draft(*args(F=300)) == ERR_UNSUPPORTED
+    assert L.medusa_mtp_draft(*args(eps=-1.0)) == ERR_ARG
+    assert L.medusa_mtp_draft(*args(h=ctypes.c_void_p(0x1004))) == ERR_ARG
+    assert L.medusa_mtp_draft(*args(ws_bytes=16)) == ERR_WORKSPACE
+    assert L.medusa_mtp_draft(None, 0, 256, 2, None, None, None, None, None, None, 256, 1e-6, None,
+                              None, None, 2, 2, 128, 10, None, 100, None, None, None, 0, None) == 0
+    assert M.medusa_mtp_workspace(1, 256, 2, 256, 2, 2, 128, 10) > 0
+    assert M.medusa_mtp_workspace(1, 256, 2, 256, 2, 2, 96, 10) == 0
