@@ -65,6 +65,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
                : "v"(g), "s"(lds_addr)
                : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once per call (the K/V
+// cache): it then displaces less of what later calls reuse (the weights) from
+// the last-level cache.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
