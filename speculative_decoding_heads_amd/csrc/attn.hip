@@ -11,8 +11,9 @@
 //   * One workgroup = one (sequence, kv head, key partition, row group).  The
 //     query rows of a kv head are all (node, q head of the group) pairs, so a
 //     KV tile brought into LDS serves every tree node and every grouped head;
-//     a row group holds up to 384 rows, so grouped-query heads normally need
-//     one workgroup per KV tile.
+//     a row group holds up to 24 16-row blocks (384 rows), and the plan sizes
+//     the groups so that their busiest SIMD carries as few blocks as the
+//     number of CUs allows.
 //   * K/V tiles stream through a 4-deep LDS ring filled by direct
 //     global->LDS loads (three tiles in flight per workgroup), non-temporal:
 //     the cache is read once per step (measured: the batch-16 verify GEMM
@@ -66,9 +67,9 @@ constexpr int kKT2 = 64;            // keys per tile
 constexpr int kNBuf = 4;            // LDS ring depth in tiles
 
 // Tree attention, bf16.  Workgroup = (sequence b, kv head g, key partition,
-// group of 128*RB query rows); 8 waves, each owning RB 16-row blocks
-// (block rb of wave w is row block 8*rb + w of the group, so short groups
-// spread over all waves).
+// group of bpg <= 8 RB 16-row blocks of query rows); 8 waves, each owning up
+// to RB blocks (block rb of wave w is block 8*rb + w of the group, so short
+// groups spread over all waves).
 //   * K and V tiles of 64 keys stream through a 4-deep LDS ring by direct
 //     global->LDS loads: three tiles are in flight while one is multiplied,
 //     with no staging registers.  Rows are stored contiguously with 16-byte
@@ -89,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seq_len,
     const uint64_t* __restrict__ anc, int anc_words, int T, int nq, int nkv, int Pmax,
-    float scale_log2, int nsplit, int rowgroups, int tiles_per_split, uint16_t* __restrict__ O,
+    float scale_log2, int nsplit, int rowgroups, int bpg, int tiles_per_split,
+    uint16_t* __restrict__ O,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   constexpr int DS = D / 32;            // MFMA steps over the head dim (S^T)
   constexpr int DB = D / 16;            // 16-wide head-dim blocks (O^T)
@@ -97,7 +99,6 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   constexpr int SWZ = CPR - 1;
   constexpr int ROWS_KB = 1024 / (2 * D);          // K/V rows per 1 KB DMA region
   constexpr int NI = kKT2 / ROWS_KB / kWaves;      // DMA issues per thread per tensor per tile
-  constexpr int ROWS_WG = 16 * RB * kWaves;
   static_assert(NI >= 1 && kKT2 % (ROWS_KB * kWaves) == 0, "tile must split into DMA regions");
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[kNBuf][kKT2 * D];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[kNBuf][kKT2 * D];
@@ -111,16 +112,19 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   const int b = bg / nkv, g = bg - b * nkv;
   const int G = nq / nkv;
   const int rows = T * G;
-  const int rows_pad = rowgroups * ROWS_WG;
+  const int rows_pad = rowgroups * bpg * 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
+  // the group's bpg <= 8 RB row blocks: block j of the group goes to slot
+  // j / 8 of wave j % 8
   int blk[RB];
   int nvb = 0;   // row blocks of this wave holding at least one real row
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    blk[rb] = rg * kWaves * RB + kWaves * rb + wave;
-    if (blk[rb] * 16 < rows) nvb = rb + 1;
+    const int j = kWaves * rb + wave;
+    blk[rb] = rg * bpg + min(j, bpg - 1);
+    if (j < bpg && blk[rb] * 16 < rows) nvb = rb + 1;
   }
 
   const int P = seq_len[b];
@@ -310,6 +314,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   // epilogue
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    if (rb >= nvb) continue;            // uniform: the slot holds no block of this group
     float l = l_run[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -450,34 +455,55 @@ __global__ __launch_bounds__(256) void tree_attn_f32(const float* __restrict__ Q
 }
 
 // ---------------------------------------------------------------- host side
-// Row blocks per wave: enough for all query rows of a kv head in one group
-// when they fit (up to 3 blocks, 384 rows).  Key partitions: one workgroup
-// fits a CU (the LDS ring), so the plan minimises (rounds of 256 workgroups)
-// x (tiles per partition), plus a small charge per partition for the merge.
+// Row groups and key partitions.  One workgroup fits a CU (the LDS ring; two
+// with the 64-wide head), and a workgroup's time per KV tile follows its
+// busiest SIMD: block j of a group sits on SIMD j % 4, so a group of bpg row
+// blocks costs about c0 + c1 ceil(bpg / 4) per tile (measured: 1.26 us with
+// two blocks on a SIMD at the 7B batch-1 shape, 2.7 us with six at the
+// 70B-layer shape).  Split keys add the merge: a launch, and the partials
+// written and read back at about 5 TB/s.  The plan cuts a kv head's row
+// blocks into equal groups of at most 24 and its keys into at most 16
+// partitions, taking the least (rounds of resident workgroups) x (tiles per
+// partition) x (tile cost) + merge; ties go to fewer groups, then to fewer
+// partitions.
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
-  AttnPlan p{1, 1, 1, 0, 1};
+  AttnPlan p{1, 1, 1, 0, 1, 1};
   if (dtype != kBF16) return p;
   const int G = nq / nkv;
   const int rows = T * G;
-  p.rb = rows <= 16 * kWaves ? 1 : rows <= 32 * kWaves ? 2 : 3;
-  const int rows_wg = 16 * kWaves * p.rb;
-  p.rowgroups = (rows + rows_wg - 1) / rows_wg;
+  const int nb = (rows + 15) / 16;                 // 16-row blocks per kv head
   const int tiles = (Pmax + kKT2 - 1) / kKT2;
-  const long base = (long)b * nkv * p.rowgroups;
-  long best = -1;
-  for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
-    const int tps = (tiles + want - 1) / want;
-    const int ns = (tiles + tps - 1) / tps;
-    const long rounds = (base * ns + 255) / 256;
-    const long cost = 2 * (rounds * tps) + (ns > 1 ? 4 + ns : 0);
-    if (best < 0 || cost < best) {
-      best = cost;
-      p.nsplit = ns;
-      p.tiles_per_split = tps;
+  const long pairs = (long)b * nkv;
+  const long per_round = d == 64 ? 512 : 256;      // workgroups resident at once
+  constexpr double c0 = 0.54, c1 = 0.36;           // us per tile
+  constexpr double merge_us = 2.5, bytes_per_us = 5e6;
+  double best = -1.0;
+  for (int groups = 1; groups <= nb; ++groups) {
+    const int bpg = (nb + groups - 1) / groups;
+    if (bpg > 3 * kWaves || (nb + bpg - 1) / bpg != groups) continue;
+    const double tile_us = c0 + c1 * ((bpg + 3) / 4);
+    for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
+      const int tps = (tiles + want - 1) / want;
+      const int ns = (tiles + tps - 1) / tps;
+      const long wgs = pairs * groups * ns;
+      const long rounds = (wgs + per_round - 1) / per_round;
+      double cost = (double)(rounds * tps) * tile_us;
+      if (ns > 1) {
+        const double partials = (double)wgs * bpg * 16 * (d * 4.0 + 8.0);
+        cost += merge_us + 2.0 * partials / bytes_per_us;
+      }
+      if (best < 0 || cost < best - 1e-9) {
+        best = cost;
+        p.bpg = bpg;
+        p.rowgroups = groups;
+        p.nsplit = ns;
+        p.tiles_per_split = tps;
+      }
     }
   }
+  p.rb = (p.bpg + kWaves - 1) / kWaves;
   if (p.nsplit > 1) {
-    const size_t rows_pad = (size_t)p.rowgroups * rows_wg;
+    const size_t rows_pad = (size_t)p.rowgroups * p.bpg * 16;
     p.ws_bytes = (size_t)b * nkv * p.nsplit * rows_pad * ((size_t)d * sizeof(float) + sizeof(float2));
   }
   return p;
@@ -496,7 +522,7 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   const int rows = T * (nq / nkv);
-  const int rows_pad = p.rowgroups * 16 * kWaves * p.rb;
+  const int rows_pad = p.rowgroups * 16 * p.bpg;
   float* ws_o = static_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + (size_t)b * nkv * p.nsplit * rows_pad * d * sizeof(float));
@@ -508,7 +534,7 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
 #define ATTN(D_, RB_)                                                                           \
   hipLaunchKernelGGL((tree_attn_bf16<D_, RB_>), dim3(nblk), dim3(kThreads), 0, st, q, k, v,     \
                      seq_len, anc, anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit,            \
-                     p.rowgroups, p.tiles_per_split, o, ws_o, ws_ml)
+                     p.rowgroups, p.bpg, p.tiles_per_split, o, ws_o, ws_ml)
   if (d == 128) {
     if (p.rb == 1) ATTN(128, 1);
     else if (p.rb == 2) ATTN(128, 2);

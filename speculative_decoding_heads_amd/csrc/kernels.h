@@ -133,6 +133,7 @@ struct AttnPlan {
   int rb;            // 16-row blocks per wave
   size_t ws_bytes;
   int tiles_per_split;  // 64-key tiles per partition
+  int bpg;           // 16-row blocks per row group (<= 8 rb)
 };
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
 // MTP draft workspace regions (byte offsets) and the attention plan it uses

@@ -340,10 +340,11 @@ def test_noalloc_attention_argument_checks():
                                       M.BF16, fake, None) == ERR_UNSUPPORTED
     assert L.medusa_tree_attn_noalloc(None, None, None, None, None, 2, 0, 65, 32, 32, 128, 2113,
                                       0.1, M.BF16, None, None) == 0
-    big = M.medusa_tree_attn_workspace(2, 65, 32, 32, 128, 2113, M.BF16)
+    # the 70B-layer shape at batch 1 (129 nodes x 8 grouped heads, prefix 8192)
+    big = M.medusa_tree_attn_workspace(1, 129, 64, 8, 128, 8192 + 129, M.BF16)
     assert big > 16 << 20
-    assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 2, 2, 65, 32, 32, 128, 2113,
-                                      0.1, M.BF16, fake, None) == ERR_UNSUPPORTED
+    assert L.medusa_tree_attn_noalloc(fake, fake, fake, fake, fake, 3, 1, 129, 64, 8, 128,
+                                      8192 + 129, 0.1, M.BF16, fake, None) == ERR_UNSUPPORTED
     assert b"scratch" in L.medusa_last_error()
 
 

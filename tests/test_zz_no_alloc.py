@@ -79,8 +79,9 @@ def test_noalloc_attention_matches_the_workspace_call():
 
 def test_noalloc_attention_refuses_partials_beyond_the_scratch():
     require_gpu()
-    # two sequences of the 7B batch-1 shape need about 30 MB of partials
-    x, shape = _case(2, (10, 10, 10, 10), 64, 32, 32, 128, 2048, 720)
+    # the 70B-layer shape at batch 1 (129 nodes x 8 grouped heads, prefix
+    # 8192) splits its keys five ways: about 21 MB of partials
+    x, shape = _case(1, (10,) * 5, 128, 64, 8, 128, 8192, 720)
     b, T, nq, nkv, d, Pmax = shape
     assert M.medusa_tree_attn_workspace(b, T, nq, nkv, d, Pmax, M.BF16) > 16 << 20
     O = torch.zeros(b, T, nq * d, dtype=torch.bfloat16, device="cuda")
