@@ -90,6 +90,15 @@ class VerifyStep:
                 raise ValueError("the MTP draft runs in bf16")
             self.ws_mtp = None          # sized on first use (the layer width comes with x)
 
+    def fit_cache(self, Pmax):
+        """Size the attention workspace for a cache of Pmax slots per (sequence,
+        kv head): the split of the keys, and with it the workspace, follows
+        the cache's capacity.  Allocates only when the current one is short."""
+        c = self.cfg
+        need = M.medusa_tree_attn_workspace(c.b, c.T, c.nq, c.nkv, c.d, Pmax, self.dt)
+        if need > self.ws_attn.numel():
+            self.ws_attn = M.workspace(need, self.device)
+
     def run(self, x, step=0, stream=None, fused=True, root_given=False):
         """Enqueue one step.  x: dict of device tensors h, W, LM, Q, Kc, Vc, seq_len.
 
@@ -210,6 +219,7 @@ class VerifyLoop:
         in place); Qs [S, b, T, nq, d],
         Kn / Vn [S, b, nkv, T, d].  after_step(s) runs after each step (eager use only)."""
         st = self.step
+        st.fit_cache(x["Kc"].shape[2])
         for s in range(Qs.shape[0]):
             M.medusa_kv_append(x["Kc"], x["Vc"], x["seq_len"], Kn[s], Vn[s], stream=stream)
             xs = dict(x)
@@ -221,6 +231,7 @@ class VerifyLoop:
 
     def capture(self, x, Qs, Kn, Vn, step0=0, root_given_first=False):
         """A torch CUDA (HIP) graph of ``run``; replaying it advances the state."""
+        self.step.fit_cache(x["Kc"].shape[2])   # no allocation under capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
