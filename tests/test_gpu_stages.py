@@ -14,6 +14,7 @@ from oracle import (heads as o_heads, lm_project, topk_stable, argmax_lowest, tr
                     tree_gather, tree_attention, accept_greedy_walk, accept_greedy_parallel,
                     accept_typical, kv_compact, counter_uniform, sample_tempered, round_bf16)
 from oracle.accept import typical_local
+from oracle.attention import tree_attention_head
 from speculative_decoding_heads_amd import medusa as M
 from tests.helpers import (TOL_BF16, TOL_F32, assert_rows_close, np64, require_gpu, say,
                            normal)
@@ -292,6 +293,46 @@ def test_tree_attention(b, k, N, nq, nkv, d, P, dt):
     ref = tree_attention(np64(Q), np64(Kc), np64(Vc), Pv, plan.anc, bf16=(dt == "bf16"))
     got = np64(O).reshape(b, T, nq, d)
     assert_rows_close(got, ref.reshape(b, T, nq, d), TOL_BF16 if dt == "bf16" else TOL_F32, "O")
+
+
+# Shapes that put the attention plan on its larger row groups (the cost model
+# picks them only with enough (sequence, kv head) pairs to fill the CUs):
+# b, k, N, nq, nkv, d, P, and the plan the model gives (blocks per group,
+# groups, key partitions) for the reader; the test checks the split decision
+# through the workspace size and every node of one q head per (sequence, kv
+# head) against the oracle.
+ATTN_PLAN_CASES = [
+    (12, (6, 5), None, 64, 8, 128, 30, True),          # 2 blocks per wave: groups of 10 + 9
+    (6, (10,) * 5, 128, 8, 8, 128, 1000, False),       # 9-block group, keys in 5 partitions
+    (12, (10,) * 4, 64, 64, 8, 128, 30, True),         # 3 blocks per wave: groups of 17 + 16
+    (12, (10,) * 4, 64, 32, 8, 128, 2000, False),      # one 17-block group, keys in 2 partitions
+    (16, (10,) * 4, 64, 64, 8, 64, 30, True),          # d 64: groups of 11, 11, 11
+    (8, (10,) * 4, 64, 32, 8, 64, 2000, False),        # d 64: groups of 9 + 8, 4 partitions
+]
+
+
+@pytest.mark.parametrize("b,k,N,nq,nkv,d,P,whole", ATTN_PLAN_CASES)
+def test_tree_attention_row_groups(b, k, N, nq, nkv, d, P, whole):
+    say("attn plan", b, k, N, nq, nkv, d, P)
+    plan = tree_plan(k, N)
+    T = plan.T
+    G = nq // nkv
+    Q, Kc, Vc, Pmax = _attn_inputs(b, T, nq, nkv, d, P, "bf16", seed=T * 17 + P + nq)
+    ws_bytes = M.medusa_tree_attn_workspace(b, T, nq, nkv, d, Pmax, M.BF16)
+    assert (ws_bytes == 0) == whole        # keys split <=> partials in the workspace
+    Pv = np.array([P - (s % 2) * min(P, 3) for s in range(b)], dtype=np.int32)
+    O = torch.empty(b, T, nq * d, dtype=Q.dtype, device=DEV)
+    M.medusa_tree_attn(Q.to(DEV), Kc.to(DEV), Vc.to(DEV), torch.from_numpy(Pv).to(DEV),
+                       _anc_words(plan).to(DEV), O, ws=M.workspace(ws_bytes))
+    torch.cuda.synchronize()
+    got = np64(O).reshape(b, T, nq, d)
+    scale = 1.0 / np.sqrt(d)
+    for s in range(b):
+        for g in range(nkv):
+            hq = g * G + (s + g) % G
+            ref = tree_attention_head(np64(Q[s, :, hq]), np64(Kc[s, g]), np64(Vc[s, g]),
+                                      int(Pv[s]), plan.anc, scale)
+            assert_rows_close(got[s, :, hq], ref, TOL_BF16, f"O seq {s} kv head {g} q head {hq}")
 
 
 def test_attention_invalid_seq_len_gives_nan_rows():
