@@ -699,14 +699,18 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
   if (logits && mb > 5 && (Kd % 64) == 0) {
     // MFMA-bound: 8-wave ring kernel.  One workgroup fits a CU, so the tile
     // (BM = 128..256 rows x BN = 256 or 320 weight rows) minimises
-    // (rounds of 256 workgroups) x (tile area); the time per unit of tile
-    // area was measured to be nearly the same across these tiles.
+    // (rounds of 256 workgroups) x (time of one round).  A round's time grows
+    // with the operand rows each workgroup streams (BM + BN slices of K) more
+    // than with its MFMA work (BM x BN): timed over six tiles at 2080 x 128256
+    // x 4096 it fits 220 (BM + BN) + BM BN (160 x 256: 2409 us; 224 x 320 and
+    // 256 x 320: 2190-2197 us).
     p.kind = 2;
     long best = -1;
     for (int wmb = 4; wmb <= 8; ++wmb)
       for (int wnb = 4; wnb <= 5; ++wnb) {
         const long tm = (M + 32 * wmb - 1) / (32 * wmb), tn = (N + 64 * wnb - 1) / (64 * wnb);
-        const long cost = ((tm * tn + 255) / 256) * (32L * wmb) * (64L * wnb);
+        const long bm = 32L * wmb, bn = 64L * wnb;
+        const long cost = ((tm * tn + 255) / 256) * (220 * (bm + bn) + bm * bn);
         if (best < 0 || cost < best || (cost == best && wmb * wnb > p.wmb * p.wnb)) {
           best = cost;
           p.wmb = wmb;
