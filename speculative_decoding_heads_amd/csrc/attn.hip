@@ -64,7 +64,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 constexpr int kWaves = 8;           // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT2 = 64;            // keys per tile
-constexpr int kNBuf = 4;            // LDS ring depth in tiles
+// LDS ring depth in tiles: 4 (three in flight, 136 KB: one workgroup per CU),
+// or 2 (one in flight, 72 KB) so that two workgroups of one 16-row block per
+// wave share a CU
 
 // Tree attention, bf16.  Workgroup = (sequence b, kv head g, key partition,
 // group of bpg <= 8 RB 16-row blocks of query rows); 8 waves, each owning up
@@ -85,7 +87,7 @@ constexpr int kNBuf = 4;            // LDS ring depth in tiles
 //     exceeds it by more than 2^8, so most tiles skip the rescale.
 //   * Key partitions write unnormalised partial outputs with (max, sum) in
 //     log2 units for attn_merge; with one partition O is written directly.
-template <int D, int RB>
+template <int D, int RB, int NBUF>
 __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seq_len,
@@ -100,8 +102,9 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   constexpr int ROWS_KB = 1024 / (2 * D);          // K/V rows per 1 KB DMA region
   constexpr int NI = kKT2 / ROWS_KB / kWaves;      // DMA issues per thread per tensor per tile
   static_assert(NI >= 1 && kKT2 % (ROWS_KB * kWaves) == 0, "tile must split into DMA regions");
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[kNBuf][kKT2 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kNBuf][kKT2 * D];
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2..4 tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[NBUF][kKT2 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[NBUF][kKT2 * D];
   __shared__ uint64_t anc_s[kMaxT * kMaxAncWords];
 
   const int tile_id = xcd_remap(blockIdx.x, gridDim.x);
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
 
   // the first tiles go out before anything else
 #pragma unroll
-  for (int i = 0; i < kNBuf - 1; ++i)
+  for (int i = 0; i < NBUF - 1; ++i)
     if (i < nt) issue(t_begin + i, i);
 
   uint4 qf[RB][DS];
@@ -295,14 +298,14 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   // real rows); the tile loop is instantiated once per block count.
   auto run_tiles = [&](auto nv_tag) {
     for (int i = 0; i < nt; ++i) {
-      // tiles issued after tile i so far: min(nt - 1 - i, kNBuf - 2), 2*NI issues each
-      const int ahead = min(nt - 1 - i, kNBuf - 2);
+      // tiles issued after tile i so far: min(nt - 1 - i, NBUF - 2), 2*NI issues each
+      const int ahead = min(nt - 1 - i, NBUF - 2);
       if (ahead >= 2) vm_wait<4 * NI>();
       else if (ahead == 1) vm_wait<2 * NI>();
       else vm_wait<0>();
       __syncthreads();   // tile i complete from every wave; tile i-1's buffer is free
-      if (i + kNBuf - 1 < nt) issue(t_begin + i + kNBuf - 1, (i + kNBuf - 1) % kNBuf);
-      if constexpr (decltype(nv_tag)::value > 0) compute(t_begin + i, i % kNBuf, nv_tag);
+      if (i + NBUF - 1 < nt) issue(t_begin + i + NBUF - 1, (i + NBUF - 1) % NBUF);
+      if constexpr (decltype(nv_tag)::value > 0) compute(t_begin + i, i % NBUF, nv_tag);
     }
   };
   __syncthreads();   // anc_s
@@ -455,49 +458,57 @@ __global__ __launch_bounds__(256) void tree_attn_f32(const float* __restrict__ Q
 }
 
 // ---------------------------------------------------------------- host side
-// Row groups and key partitions.  One workgroup fits a CU (the LDS ring; two
-// with the 64-wide head), and a workgroup's time per KV tile follows its
-// busiest SIMD: block j of a group sits on SIMD j % 4, so a group of bpg row
-// blocks costs about c0 + c1 ceil(bpg / 4) per tile (measured: 1.26 us with
-// two blocks on a SIMD at the 7B batch-1 shape, 2.7 us with six at the
-// 70B-layer shape).  Split keys add the merge: a launch, and the partials
-// written and read back at about 5 TB/s.  The plan cuts a kv head's row
-// blocks into equal groups of at most 24 and its keys into at most 16
-// partitions, taking the least (rounds of resident workgroups) x (tiles per
-// partition) x (tile cost) + merge; ties go to fewer groups, then to fewer
-// partitions.
+// Row groups, key partitions and ring depth.  With the 4-deep ring one
+// workgroup fits a CU (two with the 64-wide head), and a workgroup's time per
+// KV tile follows its busiest SIMD: block j of a group sits on SIMD j % 4, so
+// a group of bpg row blocks costs about c0 + c1 ceil(bpg / 4) per tile
+// (measured: 1.26 us with two blocks on a SIMD at the 7B batch-1 shape, 2.7 us
+// with six at the 70B-layer shape).  Groups of one block per wave (128-wide
+// head) may take the 2-deep ring instead, so that two workgroups share a CU:
+// each tile then takes about 1.7x as long but twice as many workgroups are
+// resident (7B batch 16, 512 workgroups: 171-186 us against 202-209 us).
+// Split keys add the merge: a launch, and the partials written and read back
+// at about 5 TB/s.  The plan cuts a kv head's row blocks into equal groups of
+// at most 24 and its keys into at most 16 partitions, taking the least
+// (rounds of resident workgroups) x (tiles per partition) x (tile cost) +
+// merge; ties go to the 4-deep ring, fewer groups, then fewer partitions.
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
-  AttnPlan p{1, 1, 1, 0, 1, 1};
+  AttnPlan p{1, 1, 1, 0, 1, 1, 4};
   if (dtype != kBF16) return p;
   const int G = nq / nkv;
   const int rows = T * G;
   const int nb = (rows + 15) / 16;                 // 16-row blocks per kv head
   const int tiles = (Pmax + kKT2 - 1) / kKT2;
   const long pairs = (long)b * nkv;
-  const long per_round = d == 64 ? 512 : 256;      // workgroups resident at once
   constexpr double c0 = 0.54, c1 = 0.36;           // us per tile
   constexpr double merge_us = 2.5, bytes_per_us = 5e6;
   double best = -1.0;
-  for (int groups = 1; groups <= nb; ++groups) {
-    const int bpg = (nb + groups - 1) / groups;
-    if (bpg > 3 * kWaves || (nb + bpg - 1) / bpg != groups) continue;
-    const double tile_us = c0 + c1 * ((bpg + 3) / 4);
-    for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
-      const int tps = (tiles + want - 1) / want;
-      const int ns = (tiles + tps - 1) / tps;
-      const long wgs = pairs * groups * ns;
-      const long rounds = (wgs + per_round - 1) / per_round;
-      double cost = (double)(rounds * tps) * tile_us;
-      if (ns > 1) {
-        const double partials = (double)wgs * bpg * 16 * (d * 4.0 + 8.0);
-        cost += merge_us + 2.0 * partials / bytes_per_us;
-      }
-      if (best < 0 || cost < best - 1e-9) {
-        best = cost;
-        p.bpg = bpg;
-        p.rowgroups = groups;
-        p.nsplit = ns;
-        p.tiles_per_split = tps;
+  for (int nbuf = 4; nbuf >= 2; nbuf -= 2) {
+    const long per_round = nbuf == 2 ? 512 : d == 64 ? 512 : 256;   // resident workgroups
+    const double share = nbuf == 2 ? 1.7 : 1.0;
+    for (int groups = 1; groups <= nb; ++groups) {
+      const int bpg = (nb + groups - 1) / groups;
+      if (bpg > 3 * kWaves || (nb + bpg - 1) / bpg != groups) continue;
+      if (nbuf == 2 && (d != 128 || bpg > kWaves)) continue;
+      const double tile_us = share * (c0 + c1 * ((bpg + 3) / 4));
+      for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
+        const int tps = (tiles + want - 1) / want;
+        const int ns = (tiles + tps - 1) / tps;
+        const long wgs = pairs * groups * ns;
+        const long rounds = (wgs + per_round - 1) / per_round;
+        double cost = (double)(rounds * tps) * tile_us;
+        if (ns > 1) {
+          const double partials = (double)wgs * bpg * 16 * (d * 4.0 + 8.0);
+          cost += merge_us + 2.0 * partials / bytes_per_us;
+        }
+        if (best < 0 || cost < best - 1e-9) {
+          best = cost;
+          p.bpg = bpg;
+          p.rowgroups = groups;
+          p.nsplit = ns;
+          p.tiles_per_split = tps;
+          p.nbuf = nbuf;
+        }
       }
     }
   }
@@ -531,18 +542,19 @@ hipError_t run_tree_attn(const void* Q, const void* Kc, const void* Vc, const in
   const uint16_t* k = static_cast<const uint16_t*>(Kc);
   const uint16_t* v = static_cast<const uint16_t*>(Vc);
   uint16_t* o = static_cast<uint16_t*>(O);
-#define ATTN(D_, RB_)                                                                           \
-  hipLaunchKernelGGL((tree_attn_bf16<D_, RB_>), dim3(nblk), dim3(kThreads), 0, st, q, k, v,     \
+#define ATTN(D_, RB_, NB_)                                                                     \
+  hipLaunchKernelGGL((tree_attn_bf16<D_, RB_, NB_>), dim3(nblk), dim3(kThreads), 0, st, q, k, v, \
                      seq_len, anc, anc_words, T, nq, nkv, Pmax, scale_log2, p.nsplit,            \
                      p.rowgroups, p.bpg, p.tiles_per_split, o, ws_o, ws_ml)
   if (d == 128) {
-    if (p.rb == 1) ATTN(128, 1);
-    else if (p.rb == 2) ATTN(128, 2);
-    else ATTN(128, 3);
+    if (p.rb == 1 && p.nbuf == 2) ATTN(128, 1, 2);
+    else if (p.rb == 1) ATTN(128, 1, 4);
+    else if (p.rb == 2) ATTN(128, 2, 4);
+    else ATTN(128, 3, 4);
   } else {
-    if (p.rb == 1) ATTN(64, 1);
-    else if (p.rb == 2) ATTN(64, 2);
-    else ATTN(64, 3);
+    if (p.rb == 1) ATTN(64, 1, 4);
+    else if (p.rb == 2) ATTN(64, 2, 4);
+    else ATTN(64, 3, 4);
   }
 #undef ATTN
   hipError_t e = hipGetLastError();

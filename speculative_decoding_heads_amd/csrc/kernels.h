@@ -134,6 +134,7 @@ struct AttnPlan {
   size_t ws_bytes;
   int tiles_per_split;  // 64-key tiles per partition
   int bpg;           // 16-row blocks per row group (<= 8 rb)
+  int nbuf;          // K/V tiles in the LDS ring (4, or 2: two workgroups per CU)
 };
 AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype);
 // MTP draft workspace regions (byte offsets) and the attention plan it uses

@@ -296,18 +296,25 @@ def test_tree_attention(b, k, N, nq, nkv, d, P, dt):
 
 
 # Shapes that put the attention plan on its larger row groups (the cost model
-# picks them only with enough (sequence, kv head) pairs to fill the CUs):
+# picks them only with enough (sequence, kv head) pairs to fill the CUs) and
+# on the 2-deep K/V ring (two workgroups per CU):
 # b, k, N, nq, nkv, d, P, and the plan the model gives (blocks per group,
 # groups, key partitions) for the reader; the test checks the split decision
 # through the workspace size and every node of one q head per (sequence, kv
 # head) against the oracle.
 ATTN_PLAN_CASES = [
-    (12, (6, 5), None, 64, 8, 128, 30, True),          # 2 blocks per wave: groups of 10 + 9
-    (6, (10,) * 5, 128, 8, 8, 128, 1000, False),       # 9-block group, keys in 5 partitions
-    (12, (10,) * 4, 64, 64, 8, 128, 30, True),         # 3 blocks per wave: groups of 17 + 16
-    (12, (10,) * 4, 64, 32, 8, 128, 2000, False),      # one 17-block group, keys in 2 partitions
-    (16, (10,) * 4, 64, 64, 8, 64, 30, True),          # d 64: groups of 11, 11, 11
-    (8, (10,) * 4, 64, 32, 8, 64, 2000, False),        # d 64: groups of 9 + 8, 4 partitions
+    # blocks per group x groups (last group), key partitions, ring depth
+    (12, (6, 5), None, 64, 8, 128, 30, True),          # 4 x 5 (3), whole keys, 2-deep
+    (6, (10,) * 5, 128, 8, 8, 128, 1000, False),       # 3 x 3, 3 partitions, 2-deep
+    (16, (10,) * 4, 64, 32, 32, 128, 300, True),       # 5 x 1, whole keys, 2-deep
+    (4, (1,), 0, 32, 32, 128, 2043, False),            # 1 x 1, 4 partitions, 2-deep
+    (6, (4, 3, 2), 20, 256, 32, 128, 30, True),        # 11 x 1 (2 blocks per wave), 4-deep
+    (3, (4, 3, 2), 20, 64, 8, 128, 4000, False),       # 11 x 1, 9 partitions
+    (4, (10,) * 4, 64, 256, 32, 128, 30, True),        # 17 x 2 (16; 3 blocks per wave)
+    (3, (6, 5), None, 128, 16, 128, 4000, False),      # 19 x 1, 5 partitions
+    (16, (10,) * 4, 64, 64, 8, 64, 30, True),          # d 64: 11 x 3
+    (8, (10,) * 4, 64, 32, 8, 64, 2000, False),        # d 64: 9 x 2 (8), 4 partitions
+    (2, (10,) * 4, 64, 256, 32, 64, 4000, False),      # d 64: 17 x 2 (16), 4 partitions
 ]
 
 
