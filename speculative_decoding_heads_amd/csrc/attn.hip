@@ -464,9 +464,12 @@ __global__ __launch_bounds__(256) void tree_attn_f32(const float* __restrict__ Q
 // a group of bpg row blocks costs about c0 + c1 ceil(bpg / 4) per tile
 // (measured: 1.26 us with two blocks on a SIMD at the 7B batch-1 shape, 2.7 us
 // with six at the 70B-layer shape).  Groups of one block per wave (128-wide
-// head) may take the 2-deep ring instead, so that two workgroups share a CU:
-// each tile then takes about 1.7x as long but twice as many workgroups are
-// resident (7B batch 16, 512 workgroups: 171-186 us against 202-209 us).
+// head) may take the 2-deep ring instead: alone on a CU its tiles cost about
+// 0.93x (the first tile lands sooner when each workgroup asks for one, not
+// three: 7B batch 1, 18.8 against 20.2 us), and two workgroups can share a
+// CU, each tile then taking about 1.7x as long with twice as many workgroups
+// resident (7B batch 16, 512 workgroups: 170-186 us against 199-226 us).
+// Two or three blocks per wave gain nothing from it (70B layer, 128k).
 // Split keys add the merge: a launch, and the partials written and read back
 // at about 5 TB/s.  The plan cuts a kv head's row blocks into equal groups of
 // at most 24 and its keys into at most 16 partitions, taking the least
@@ -485,18 +488,18 @@ AttnPlan attn_plan(int b, int T, int nq, int nkv, int d, int Pmax, int dtype) {
   double best = -1.0;
   for (int nbuf = 4; nbuf >= 2; nbuf -= 2) {
     const long per_round = nbuf == 2 ? 512 : d == 64 ? 512 : 256;   // resident workgroups
-    const double share = nbuf == 2 ? 1.7 : 1.0;
     for (int groups = 1; groups <= nb; ++groups) {
       const int bpg = (nb + groups - 1) / groups;
       if (bpg > 3 * kWaves || (nb + bpg - 1) / bpg != groups) continue;
       if (nbuf == 2 && (d != 128 || bpg > kWaves)) continue;
-      const double tile_us = share * (c0 + c1 * ((bpg + 3) / 4));
+      const double tile_us = c0 + c1 * ((bpg + 3) / 4);
       for (int want = 1; want <= kMaxSplit && want <= tiles; ++want) {
         const int tps = (tiles + want - 1) / want;
         const int ns = (tiles + tps - 1) / tps;
         const long wgs = pairs * groups * ns;
         const long rounds = (wgs + per_round - 1) / per_round;
-        double cost = (double)(rounds * tps) * tile_us;
+        const double share = nbuf == 4 ? 1.0 : wgs <= 256 ? 0.93 : 1.7;
+        double cost = (double)(rounds * tps) * tile_us * share;
         if (ns > 1) {
           const double partials = (double)wgs * bpg * 16 * (d * 4.0 + 8.0);
           cost += merge_us + 2.0 * partials / bytes_per_us;

@@ -305,9 +305,9 @@ def test_tree_attention(b, k, N, nq, nkv, d, P, dt):
 ATTN_PLAN_CASES = [
     # blocks per group x groups (last group), key partitions, ring depth
     (12, (6, 5), None, 64, 8, 128, 30, True),          # 4 x 5 (3), whole keys, 2-deep
-    (6, (10,) * 5, 128, 8, 8, 128, 1000, False),       # 3 x 3, 3 partitions, 2-deep
+    (2, (10,) * 5, 128, 8, 8, 128, 2000, False),       # 3 x 3, 5 partitions, 2-deep
     (16, (10,) * 4, 64, 32, 32, 128, 300, True),       # 5 x 1, whole keys, 2-deep
-    (4, (1,), 0, 32, 32, 128, 2043, False),            # 1 x 1, 4 partitions, 2-deep
+    (4, (1,), 0, 32, 32, 128, 2043, False),            # 1 x 1, 2 partitions, 2-deep
     (6, (4, 3, 2), 20, 256, 32, 128, 30, True),        # 11 x 1 (2 blocks per wave), 4-deep
     (3, (4, 3, 2), 20, 64, 8, 128, 4000, False),       # 11 x 1, 9 partitions
     (4, (10,) * 4, 64, 256, 32, 128, 30, True),        # 17 x 2 (16; 3 blocks per wave)
