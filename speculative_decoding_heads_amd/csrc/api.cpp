@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -498,7 +499,10 @@ static int attn_check(int32_t b, int32_t T, int32_t nq, int32_t nkv, int32_t d, 
     return fail(MEDUSA_ERR_UNSUPPORTED, "f32 attention supports d <= 256");
   if (dtype == MEDUSA_F32 && Pmax > 16384)
     return fail(MEDUSA_ERR_UNSUPPORTED, "f32 attention supports Pmax <= 16384");
-  if ((int64_t)b * nkv * ((Pmax + 63) / 64) * ((T * (nq / nkv) + 63) / 64) > INT32_MAX / 4)
+  // the plan's grid is (sequence, kv head) x row groups (at most one per
+  // 16-row block) x key partitions (at most 16 and at most one per 64 keys)
+  if ((int64_t)b * nkv * std::min((Pmax + 63) / 64, 16) * ((T * (nq / nkv) + 15) / 16) >
+      INT32_MAX / 4)
     return fail(MEDUSA_ERR_UNSUPPORTED, "attention grid too large");
   if (dtype == MEDUSA_F32 && (int64_t)b * T * nq > INT32_MAX / 2)
     return fail(MEDUSA_ERR_UNSUPPORTED, "attention grid too large");

@@ -112,6 +112,10 @@ def test_validation_before_launch():
                               None, 0, None) == ERR_ARG
     assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 1, 1, 300, 4, 4, 128, 400, 0.1, 1, fake,
                               None, 0, None) == ERR_ARG
+    # a grid beyond the launch's 32-bit workgroup count is refused before any launch
+    assert L.medusa_tree_attn(fake, fake, fake, fake, fake, 2, 1 << 20, 65, 32, 32, 128, 2113, 0.1,
+                              1, fake, None, 0, None) == ERR_UNSUPPORTED
+    assert b"grid" in L.medusa_last_error()
     # accept: bad mode, typical / rejection without temperature, small workspace
     assert L.medusa_accept(fake, fake, fake, fake, 1, 5, 10, 2, 4, 1.0, 0.3, 0.09, 0, 0, fake, fake,
                            fake, fake, fake, 1 << 20, None) == ERR_ARG
