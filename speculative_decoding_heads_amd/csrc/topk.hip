@@ -210,23 +210,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
       }
     }
   };
-  if (in_regs) {
+  // Only a lane whose own largest value reaches tau's value can hold a
+  // candidate (a handful of lanes for continuous data): the others skip the
+  // pass, and with it the re-read of long rows.
+  if (li >= 0 && lv >= tv) {
+    if (in_regs) {
 #pragma unroll
-    for (int u = 0; u < kTopkKPT / 4; ++u) {
-      const int e = u * kTopkThreads + tid;
-      if (e < nv) {
+      for (int u = 0; u < kTopkKPT / 4; ++u) {
+        const int e = u * kTopkThreads + tid;
+        if (e < nv) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) offer(v[u][q], 4 * e + q);
+          for (int q = 0; q < 4; ++q) offer(v[u][q], 4 * e + q);
+        }
       }
-    }
-  } else if (vec) {
-    for (int e = tid; e < nv; e += kTopkThreads) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(x + 4 * e);
+    } else if (vec) {
+      for (int e = tid; e < nv; e += kTopkThreads) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(x + 4 * e);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) offer(w[q], 4 * e + q);
+        for (int q = 0; q < 4; ++q) offer(w[q], 4 * e + q);
+      }
+    } else {
+      for (int e = tid; e < a.V; e += kTopkThreads) offer(x[e], e);
     }
-  } else {
-    for (int e = tid; e < a.V; e += kTopkThreads) offer(x[e], e);
   }
   __syncthreads();
   const int nc = ncand;
