@@ -113,7 +113,13 @@ def test_head_rows_and_base_rows_differ_only_in_summation_order(b, H, V):
                                        (80, 128, 30720), (5, 256, 40000), (65, 128, 50000),
                                        (16, 256, 60000), (161, 128, 40001),
                                        (1040, 384, 3333), (97, 256, 32000), (129, 384, 5000),
-                                       (150, 256, 31000), (160, 128, 128256)])
+                                       (150, 256, 31000), (160, 128, 128256),
+                                       # one ragged shape per remaining ring-GEMM tile:
+                                       # 160x320, 192x256, 192x320, 224x256, 224x320,
+                                       # 256x256, 256x320 (rows x weight rows)
+                                       (257, 256, 40001), (321, 384, 32000), (321, 256, 40001),
+                                       (385, 384, 32000), (385, 128, 40001), (449, 256, 32000),
+                                       (449, 128, 40001)])
 def test_verify_rows_projection(rows, H, V):
     dt = torch.float32 if rows == 11 else torch.bfloat16
     x = normal((rows, H), rows, 1.0, dt)
