@@ -487,8 +487,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 // Tile BM = 32*WMB activation rows x BN = 16*WNB*NWN weight rows; waves 2
 // (along M) x NWN (along N), each 16*WMB x 16*WNB outputs.  The operands
 // stream in 32-wide K slices through a 4-deep LDS ring filled by direct
-// global->LDS loads: three slices are in flight while one is multiplied, with
-// no staging registers.  A slice row is 64 bytes; its four 16-byte chunks are
+// global->LDS loads: while one slice is multiplied the next two are in
+// flight and the third is issued, with no staging registers.  A slice row is 64 bytes; its four 16-byte chunks are
 // XOR-swizzled by (row >> 1) & 3.  A fragment read has lanes 16 apart read two
 // chunks of the same row; with this swizzle the rows and chunks that the LDS
 // serves together land on distinct banks (bank-conflict counters read zero;
@@ -496,11 +496,15 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 // of its busy time).  One barrier per slice.
 // Each DMA issue fills a 1 KB region (16 rows x 64 bytes).  A ring slot holds
 // the activation rows followed by the weight rows, so the BM/16 + BN/16
-// regions of a slice are numbered once and dealt round-robin to the waves:
-// the first (regions mod waves) waves issue one more than the rest and wait on
-// their own count.  (Padding every wave to the same count, as with separate
-// activation and weight rings, asked the L2 for 15% more requests at 224 x
-// 320, rewriting identical bytes.)
+// regions of a slice are numbered once and dealt round-robin to the first
+// wave of each SIMD (waves 0..NW/2-1; the first (regions mod NW/2) of them
+// issue one more and wait on their own count).  Those waves issue after the
+// slice's MFMAs: the 30-odd loads of a slice take a few hundred cycles to
+// issue (the CU's vector-memory path accepts about one 1 KB load per 15
+// cycles), and issued right after the barrier they kept every SIMD's MFMA
+// pipe idle meanwhile; the SIMD's first wave gets the pipe first, so its loads
+// now go out while the second wave's MFMAs run, and the slot they fill was
+// read before this slice's barrier.
 template <int WMB, int WNB, int NWN, class Epi>
 __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __restrict__ X,
                                                            int64_t ldx, int M,
@@ -509,7 +513,8 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   constexpr int NW = 2 * NWN;                        // waves: 2 along M x NWN along N
   constexpr int BM = 32 * WMB, BN = 16 * WNB * NWN, BK = 32, NS = 4;
   constexpr int XR = BM / 16, R = XR + BN / 16;      // 1 KB regions per slice
-  constexpr int DLO = R / NW, DHI = (R + NW - 1) / NW;  // DMA issues per wave per slice
+  constexpr int NI = NW / 2;                         // issuing waves: the first on each SIMD
+  constexpr int DLO = R / NI, DHI = (R + NI - 1) / NI;  // DMA issues per issuing wave and slice
   constexpr int SL = (BM + BN) * BK;                 // one ring slot, elements
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS][SL];
 
@@ -523,12 +528,13 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   const int nk = Kd / BK;
 
   // region q < XR: activation rows 16q..16q+15, else weight rows 16(q-XR)..
-  const bool extra = wave < R % NW;                  // this wave issues DHI regions
+  const bool issuer = wave < NI;
+  const bool extra = issuer && wave < R % NI;        // this wave issues DHI regions
   const uint16_t* src[DHI];
   uint32_t off[DHI];
 #pragma unroll
   for (int j = 0; j < DHI; ++j) {
-    const int q = min(wave + NW * j, R - 1);
+    const int q = min(wave % NI + NI * j, R - 1);
     const int row = 16 * (q < XR ? q : q - XR) + (lane >> 2);
     const int ch = (lane & 3) ^ ((row >> 1) & 3);
     src[j] = q < XR ? X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ch
@@ -537,6 +543,7 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
   }
   const uint32_t rl = lds_u32(&ring[0][0]);
   auto issue = [&](int kt, int buf) {
+    if (!issuer) return;
     const int k0 = kt * BK;
     const uint32_t base = rl + (uint32_t)(buf * SL * 2);
 #pragma unroll
@@ -576,7 +583,7 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
     if (i < nk) issue(i, i);
   for (int kt = 0; kt < nk; ++kt) {
     // slices issued after slice kt so far: min(nk - 1 - kt, NS - 2), DHI or
-    // DLO issues each
+    // DLO issues each (none outstanding on the waves that do not issue)
     const int ahead = min(nk - 1 - kt, NS - 2);
     if (DHI > DLO && extra) {
       if (ahead >= 2) vm_wait<2 * DHI>();
@@ -588,8 +595,8 @@ __global__ __launch_bounds__(128 * NWN) void gemm_ring_bf16(const uint16_t* __re
       else vm_wait<0>();
     }
     __syncthreads();   // slice kt complete from every wave; slice kt-1's buffer is free
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
     compute(kt % NS);
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
   }
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb)
