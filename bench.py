@@ -414,11 +414,53 @@ def copy_calibration(mib):
     del src, dst
 
 
+def stream_read_rates(sizes, copies=3, iters=30, log=print):
+    """The library's plain-read yardstick (medusa_stream_read) on buffers of the
+    given byte counts: median rate over `iters` calls, each call timed by
+    events on the launch stream, `copies` buffers rotated so the last-level
+    cache cannot serve a repeat.  Returns {bytes: GB/s}."""
+    import torch
+    from speculative_decoding_heads_amd import medusa as M
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for nbytes in sorted(set(sizes)):
+        n16 = (nbytes + 15) // 16
+        bufs = [torch.ones(n16 * 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+        for i in range(6):
+            M.medusa_stream_read(bufs[i % copies], sink)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            M.medusa_stream_read(bufs[i % copies], sink)
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        out[nbytes] = round(n16 * 16 / ts[len(ts) // 2] / 1e9, 1)
+        del bufs
+        torch.cuda.empty_cache()
+    log(f"stream read yardstick (GB/s by bytes): {out}")
+    return out
+
+
+def attach_read_yardstick(block, rates):
+    """Each HBM-bound roofline entry gets the yardstick's rate for a read of its
+    algorithmic bytes and its achieved rate as a fraction of that."""
+    for entry in [block.get("roofline")] + list((block.get("rooflines") or {}).values()):
+        if not entry or entry.get("bound") != "hbm":
+            continue
+        r = rates.get(entry["alg_bytes_per_launch"])
+        if r:
+            entry["read_yardstick_GBps"] = r
+            entry["frac_of_read_yardstick"] = round(entry["achieved"] / r, 4)
+
+
 def measured_peaks(log=print):
     """Achievable reference rates on this GPU, reported next to the spec-sheet
     peaks: a 1 GiB device copy (read + write bytes), a 1 GiB reduction (read
-    bytes) and a vendor bf16 GEMM (8192 x 8192 x 8192, library call).  These
-    use torch/library kernels only as yardsticks; no part of the step does."""
+    bytes), a vendor bf16 GEMM (8192 x 8192 x 8192, library call), and the
+    library's plain-read yardstick at 1 GiB.  The torch and vendor kernels are
+    yardsticks only; no part of the step uses them."""
     import torch
     def timed(fn, iters):
         fn()
@@ -443,6 +485,7 @@ def measured_peaks(log=print):
     t_mm = timed(lambda: torch.matmul(a, b), 10)
     del a, b
     out = {"copy_GBps": round(2 * n / t_copy / 1e9, 1), "read_GBps": round(n / t_read / 1e9, 1),
+           "stream_read_1GiB_GBps": stream_read_rates([1 << 30], log=log)[1 << 30],
            "vendor_bf16_gemm_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
            "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_TFLOPs": BF16_PEAK_TFLOPS}
     log(f"measured peaks: {out}")
@@ -554,6 +597,15 @@ def main():
         out["tree_sweep"] = tree_sweep(cfg, sizes, args.steps, args.warmup, log)
     torch.cuda.synchronize()
     out["measured_peaks"] = None if args.no_peaks else measured_peaks(log)
+    if not args.no_peaks:
+        # the plain-read yardstick at the byte counts of every HBM-bound call
+        blocks = [out] + [out[k] for k in ("also", "large") if k in out]
+        sizes = [e["alg_bytes_per_launch"] for blk in blocks
+                 for e in (blk.get("rooflines") or {}).values() if e.get("bound") == "hbm"]
+        rates = stream_read_rates(sizes, log=log)
+        out["measured_peaks"]["stream_read_GBps_by_bytes"] = {str(k): v for k, v in rates.items()}
+        for blk in blocks:
+            attach_read_yardstick(blk, rates)
     out["cpu_baseline"] = None if args.no_cpu_baseline else \
         cpu_baseline(cfg, args.cpu_seconds, args.cpu_single_seconds, log)
     print(json.dumps(out), flush=True)

@@ -519,6 +519,23 @@ int medusa_mtp_draft(const void* h, int32_t b, int32_t H, int32_t K, const void*
                      const void* LM, int32_t V, void* u_out, float* logits, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * medusa_stream_read - a plain read of a device buffer, computing nothing of
+ * the method: the yardstick for the weight streams.  [deep-dive] "What it
+ * costs on a CPU-bound SLM": the step's pace is set by the memory traffic of
+ * the weight reads; timing this call on a buffer of a weight stream's size
+ * gives the read rate the part reaches for that many bytes.
+ *   buf    device, `bytes` readable, 16-byte aligned; bytes a multiple of 16
+ *          (bytes == 0 launches nothing)
+ *   never  a 32-bit value; each thread folds the 32-bit words it read by
+ *          XOR and writes `never` to sink[0] (device, 4 bytes) only when its
+ *          fold equals `never`, so the loads cannot be elided; with a value
+ *          no fold takes nothing is written
+ * Returns MEDUSA_ERR_ARG for a NULL or misaligned pointer or a size that is
+ * not a multiple of 16.
+ * ------------------------------------------------------------------------- */
+int medusa_stream_read(const void* buf, size_t bytes, uint32_t never, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -742,4 +742,16 @@ int medusa_accept_tally(const int32_t* L, const int32_t* path, int32_t b, const 
                     "accept_tally");
 }
 
+// ------------------------------------------------------------------- yardstick
+int medusa_stream_read(const void* buf, size_t bytes, uint32_t never, void* sink, void* stream) {
+  if (bytes % 16) return fail(MEDUSA_ERR_ARG, "stream_read: bytes must be a multiple of 16");
+  if (bytes == 0) return MEDUSA_OK;
+  if (!buf || !sink) return fail(MEDUSA_ERR_ARG, "NULL pointer");
+  if (!aligned16(buf) || ((uintptr_t)sink & 3))
+    return fail(MEDUSA_ERR_ARG, "stream_read: buf must be 16-byte and sink 4-byte aligned");
+  return hip_status(run_stream_read(buf, bytes, never, static_cast<uint32_t*>(sink),
+                                    as_stream(stream)),
+                    "stream_read");
+}
+
 }  // extern "C"

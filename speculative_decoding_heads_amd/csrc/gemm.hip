@@ -15,7 +15,7 @@
 // are the MFMA "A" rows, X rows the "B" columns, so each lane ends up with 4
 // consecutive n of one output row (one 16-byte store of logits).
 //
-// Three bf16 kernels:
+// Four bf16 kernels:
 //   gemm_skinny : M <= 16 with fewer than 30720 weight rows.  HBM-bound weight
 //                 stream.  A workgroup owns 16*NB weight rows; its 4 waves
 //                 split K and reduce through LDS.  Both operands go global ->
@@ -30,6 +30,10 @@
 //                 starts its K walk at its own chunk, so the workgroups do not
 //                 all read the same slice of X at once.  Tiles are mapped to
 //                 XCDs so that the M-tiles of one weight tile run on one XCD.
+//   gemm_dma    : the logits GEMMs of gemm_tiled's 8-wave shapes (at most 80
+//                 rows over a wide vocabulary: the heads' LM pass, the batch-1
+//                 verify rows): the same tile and MFMA order, with both
+//                 operands streamed global -> LDS by DMA (see below).
 //   gemm_ring   : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
@@ -498,6 +502,159 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
   }
 }
 
+// ---------------------------------------------------------------- weight stream by LDS DMA
+// The logits GEMMs of at most 80 rows over a wide vocabulary (the heads' LM
+// pass, the batch-1 verify rows): the same tile as gemm_tiled_bf16 (BM =
+// 16*MB activation rows shared by NW waves of 16 weight rows each, the
+// rotated K walk, the same MFMA order, so the same logits bit for bit), but
+// both operands reach LDS by direct global->LDS loads through an NBUF-deep
+// ring of 128-wide K chunks instead of through registers.  Measured on a
+// plain read of 262 MB: 45.8 us into registers, 40.7 us by LDS DMA with the
+// non-temporal hint, 45.4 us without it (1 GiB: 6.0, 7.0 and 6.0 TB/s).
+//   * A ring slot holds the chunk's X rows and then each wave's 16 weight
+//     rows, both row-major with their 16-byte pieces XOR-swizzled by row (as
+//     the tiled kernel's X), so the fragment reads are free of bank
+//     conflicts; each DMA issue covers four whole 256-byte chunk rows (a
+//     gather of 16-byte pieces 64 bytes apart, one fragment's worth, ran at
+//     half the rate).
+//   * X units (four rows each) are dealt round-robin to the waves; a wave
+//     past the last unit repeats one (the same bytes to the same place), so
+//     every wave issues XI + 4 loads per chunk and waits on one count.  One
+//     barrier per chunk.
+//   * w_nt: the weights with the non-temporal hint.  The heads' LM pass
+//     reads them without it, so the verify pass over the same weights finds
+//     much of them in the last-level cache; the verify pass, the last reader
+//     in the step, streams them non-temporally (7B batch 1: the LM pass 51 ->
+//     47 us, the verify pass 48 -> 41.5 us).  X is re-read by every
+//     workgroup from L2 and never takes the hint.
+template <int MB, class Epi, int NW, int NBUF>
+__global__ __launch_bounds__(64 * NW) void gemm_dma_bf16(const uint16_t* __restrict__ X,
+                                                         int64_t ldx, int M,
+                                                         const uint16_t* __restrict__ W, int N,
+                                                         int Kd, int ntm, Epi epi, bool rev,
+                                                         bool w_nt) {
+  constexpr int NT = 64 * NW;
+  constexpr int BM = 16 * MB;
+  constexpr int BN = 16 * NW;
+  constexpr int LDSROW = 128;                      // bf16 per chunk row
+  constexpr int XU = BM / 4;                       // 1 KB X units per chunk
+  constexpr int XI = (XU + NW - 1) / NW;           // X issues per wave and chunk
+  constexpr int NI = XI + 4;                       // loads per wave and chunk
+  constexpr int SLOT = (BM + BN) * LDSROW;         // elements per ring slot
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2..4 chunks");
+  auto xsw = [](int r) { return (r & 3) | ((r & 4) << 1); };
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NBUF * SLOT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int tm = t % ntm, tn = t / ntm;
+  const int m0 = tm * BM, n0 = tn * BN + wave * 16;
+  const int nchunks = Kd >> 7;
+
+  // lane l of a unit: row 4u + l/16 of the unit's four, slot l%16 of that
+  // row, which holds piece (l%16) ^ xsw(row)
+  const int urow = lane >> 4;
+  const uint16_t* xsrc[XI];
+  uint32_t xoff[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int u = (i * NW + wave) % XU;
+    const int row = 4 * u + urow;
+    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * ((lane & 15) ^ xsw(row));
+    xoff[i] = (uint32_t)(u * 1024);
+  }
+  const uint16_t* wsrc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 4 * u + urow;
+    wsrc[u] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ((lane & 15) ^ xsw(row));
+  }
+  const uint32_t wreg = (uint32_t)((BM + 16 * wave) * LDSROW * 2);
+  const uint32_t rl = lds_u32(&ring[0]);
+  // rotated K walk, as in gemm_tiled_bf16 (rev: backwards from the same chunk)
+  const int rot = (int)(blockIdx.x % (unsigned)nchunks);
+  auto rc = [&](int c) {
+    if (rev) { const int q = rot - 1 - c; return q < 0 ? q + nchunks : q; }
+    const int q = c + rot;
+    return q >= nchunks ? q - nchunks : q;
+  };
+  auto issue = [&](int c, int buf) {
+    const int k0 = rc(c) << 7;
+    const uint32_t base = rl + (uint32_t)(buf * SLOT * 2);
+#pragma unroll
+    for (int i = 0; i < XI; ++i) dma16(xsrc[i] + k0, __builtin_amdgcn_readfirstlane(base + xoff[i]));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t l = __builtin_amdgcn_readfirstlane(base + wreg + (uint32_t)(u * 1024));
+      if (w_nt) dma16_nt(wsrc[u] + k0, l);
+      else dma16(wsrc[u] + k0, l);
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = xsw(r16);
+  auto compute = [&](int buf) {
+    const uint16_t* xb = &ring[buf * SLOT + r16 * LDSROW];
+    const uint16_t* wb = &ring[buf * SLOT + (BM + 16 * wave + r16) * LDSROW];
+    uint4 w[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) w[s] = *reinterpret_cast<const uint4*>(wb + 8 * ((4 * g4 + s) ^ sw));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint4 b = *reinterpret_cast<const uint4*>(xb + mb * 16 * LDSROW + 8 * ((4 * g4 + s) ^ sw));
+        acc[mb] = mfma16x16x32(w[s], b, acc[mb]);
+      }
+  };
+
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nchunks) issue(i, i);
+  for (int c = 0; c < nchunks; ++c) {
+    const int ahead = min(nchunks - 1 - c, NBUF - 2);   // chunks issued after chunk c
+    if (ahead >= 2) vm_wait<2 * NI>();
+    else if (ahead == 1) vm_wait<NI>();
+    else vm_wait<0>();
+    __syncthreads();   // chunk c landed from every wave; chunk c-1's slot is free
+    if (c + NBUF - 1 < nchunks) issue(c + NBUF - 1, (c + NBUF - 1) % NBUF);
+    compute(c % NBUF);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 4 * g4, acc[mb]);
+  if constexpr (HasParts<Epi>::value) {
+    // row partials over this workgroup's BN columns, as in gemm_tiled_bf16
+    __syncthreads();                        // every wave is past its last read of the ring
+    RowPart* red = reinterpret_cast<RowPart*>(&ring[0]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float v[4];
+      int col[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = acc[mb][i];
+        col[i] = n0 + 4 * g4 + i;
+      }
+      RowPart pt = lane_part(v, col, N, epi.typical, epi.inv_temp);
+      part_xor(pt, 16, epi.typical);
+      part_xor(pt, 32, epi.typical);
+      if (g4 == 0) red[wave * BM + 16 * mb + r16] = pt;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+      if (m0 + r >= M) continue;
+      RowPart pt = red[r];
+      for (int w = 1; w < NW; ++w) part_merge(pt, red[w * BM + r], epi.typical);
+      epi.write_part(m0 + r, tn, pt);
+    }
+    epi.write_header();
+  }
+}
+
 // ---------------------------------------------------------------- MFMA-bound, LDS ring
 // Tile BM = 32*WMB activation rows x BN = 16*WNB*NWN weight rows; waves 2
 // (along M) x NWN (along N), each 16*WMB x 16*WNB outputs.  The operands
@@ -770,7 +927,7 @@ static Bf16Plan plan_bf16(int M, int N, int Kd, bool logits, bool skinny_ok) {
 template <class Epi>
 static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint16_t* W, int N,
                               int Kd, const Epi& epi, hipStream_t st, bool rev = false,
-                              int batch = 1, int64_t bsx = 0, int64_t bsw = 0) {
+                              int batch = 1, int64_t bsx = 0, int64_t bsw = 0, bool w_nt = false) {
   // logits always take the tiled / ring kernels, so the verify-rows logits of
   // medusa_heads and medusa_verify_logits come from the same kernel
   const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
@@ -809,6 +966,24 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
 #undef RING
     return hipGetLastError();
   }
+  // logits over a wide vocabulary from at most 80 rows in 8-wave workgroups:
+  // the weight stream by LDS DMA (one problem per launch)
+  if constexpr (IsLogits<Epi>::value)
+    if (p.nw == 8 && p.mb <= 5 && batch == 1 && (N % 128) == 0) {
+      const int ntm = (M + 16 * p.mb - 1) / (16 * p.mb);
+#define DMAK(MB_)                                                                                 \
+  hipLaunchKernelGGL((gemm_dma_bf16<MB_, Epi, 8, 3>), dim3(ntm * p.ntiles), dim3(512), 0, st, X,  \
+                     ldx, M, W, N, Kd, ntm, epi, rev, w_nt)
+      switch (p.mb) {
+        case 1: DMAK(1); break;
+        case 2: DMAK(2); break;
+        case 3: DMAK(3); break;
+        case 4: DMAK(4); break;
+        default: DMAK(5); break;
+      }
+#undef DMAK
+      return hipGetLastError();
+    }
 #define TILED_NW(MB_, NW_)                                                                     \
   do {                                                                                         \
     const int ntm = (M + 16 * MB_ - 1) / (16 * MB_);                                           \
@@ -875,11 +1050,11 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
 }
 
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st, bool rev, int64_t ldc) {
+                         float* logits, hipStream_t st, bool rev, int64_t ldc, bool stream_w) {
   EpiLogits epi{logits, ldc > 0 ? ldc : (int64_t)V, M, V};
   if (dtype == kBF16)
     return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
-                       H, epi, st, rev);
+                       H, epi, st, rev, 1, 0, 0, stream_w);
   return launch_f32(static_cast<const float*>(x), H, M, static_cast<const float*>(LM), V, H, epi,
                     st);
 }
@@ -958,7 +1133,9 @@ size_t verify_workspace(int M, int N, int Kd, int dtype, int mode) {
 
 hipError_t run_verify_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
                              float* logits, int mode, float temperature, void* ws, hipStream_t st) {
-  if (!verify_uses_parts(M, V)) return run_lm_logits(x, M, H, LM, V, dtype, logits, st);
+  // the verify pass is the step's last reader of the LM weights: they stream
+  // non-temporally where the weight-stream kernel runs
+  if (!verify_uses_parts(M, V)) return run_lm_logits(x, M, H, LM, V, dtype, logits, st, false, 0, true);
   const bool typical = mode == kTypical;
   const float inv_temp = 1.0f / temperature;
   int* header = static_cast<int*>(ws);
@@ -977,7 +1154,7 @@ hipError_t run_verify_logits(const void* x, int M, int H, const void* LM, int V,
     epi.pkey = pkey;
     epi.pstat = pstat;
     return launch_bf16(static_cast<const uint16_t*>(x), H, M, static_cast<const uint16_t*>(LM), V,
-                       H, epi, st);
+                       H, epi, st, false, 1, 0, 0, true);
   }
   hipError_t e = run_lm_logits(x, M, H, LM, V, dtype, logits, st);
   if (e != hipSuccess) return e;

@@ -22,8 +22,12 @@ hipError_t run_heads_hidden(const void* x, int M, int H, const void* W, int n_he
 // rev: the weight-streaming kernel walks K backwards (same products, another
 // summation order); see medusa_heads.
 // ldc: logits row stride in floats (0: V).
+// stream_w: the weights are read with the non-temporal hint where the
+// weight-stream kernel runs (for the last pass over them in a step); the
+// logits are the same either way.
 hipError_t run_lm_logits(const void* x, int M, int H, const void* LM, int V, int dtype,
-                         float* logits, hipStream_t st, bool rev = false, int64_t ldc = 0);
+                         float* logits, hipStream_t st, bool rev = false, int64_t ldc = 0,
+                         bool stream_w = false);
 // LM projection of the verify rows plus acceptance partials per (row, weight
 // tile) in ws: a header (kPartsHeader bytes, the int32 fields below), then
 // [rows][ntiles] argmax keys (u64, greedy) or RowStat (typical).  The header
@@ -182,5 +186,9 @@ hipError_t run_accept_tally(const int* L, const int* path, int b, int K, const T
 
 hipError_t run_kv_compact(void* Kc, void* Vc, int* seq_len, const int* path, const int* L, int b,
                           int nkv, int Pmax, int d, int K, int dtype, hipStream_t st);
+
+// ---- yardstick (probe.hip): a plain read of `bytes` (a multiple of 16)
+hipError_t run_stream_read(const void* buf, size_t bytes, uint32_t never, uint32_t* sink,
+                           hipStream_t st);
 
 }  // namespace medusa

@@ -82,6 +82,7 @@ _SIGS = {
     "medusa_hydra_draft": ([_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32,
                             _F, _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P],
                            _I32),
+    "medusa_stream_read": ([_P, _SZ, ctypes.c_uint32, _P, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -570,6 +571,18 @@ def medusa_next_hidden(O, path, L, h, stream=None):
     st = lib().medusa_next_hidden(_ptr(O), _ptr(path), _ptr(L), b, T, K, H, dtype_code(O), _ptr(h),
                                   _stream(stream))
     _check("medusa_next_hidden", st)
+
+
+def medusa_stream_read(buf, sink, never=0x9E3779B9, stream=None):
+    """Plain read of the whole of `buf` (a device tensor, 16-byte multiple):
+    the yardstick for the weight streams.  Each thread folds the 32-bit words
+    it read by XOR and writes `never` to sink (a 4-byte device tensor) only
+    when its fold equals it."""
+    _need(buf.is_contiguous(), "buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    _need(sink.numel() * sink.element_size() >= 4, "sink: expected at least 4 bytes")
+    st = lib().medusa_stream_read(_ptr(buf), nbytes, never & 0xFFFFFFFF, _ptr(sink), _stream(stream))
+    _check("medusa_stream_read", st)
 
 
 def medusa_hydra_workspace(b, H, V, k, kmax, plan_parent, plan_rank):

@@ -372,3 +372,14 @@ def test_mtp_draft_argument_checks():
                               None, None, 2, 2, 128, 10, None, 100, None, None, None, 0, None) == 0
     assert M.medusa_mtp_workspace(1, 256, 2, 256, 2, 2, 128, 10) > 0
     assert M.medusa_mtp_workspace(1, 256, 2, 256, 2, 2, 96, 10) == 0
+
+
+def test_stream_read_argument_checks():
+    L = M.lib()
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+    assert L.medusa_stream_read(fake, 24, 0, fake, None) == ERR_ARG          # not a 16-byte multiple
+    assert L.medusa_stream_read(None, 16, 0, fake, None) == ERR_ARG          # NULL buffer
+    assert L.medusa_stream_read(fake, 16, 0, None, None) == ERR_ARG          # NULL sink
+    assert L.medusa_stream_read(ctypes.c_void_p(0x1008), 16, 0, fake, None) == ERR_ARG   # misaligned
+    assert L.medusa_stream_read(ctypes.c_void_p(0x1000), 16, 0, ctypes.c_void_p(0x1002), None) == ERR_ARG
+    assert L.medusa_stream_read(None, 0, 0, None, None) == 0                 # nothing to read

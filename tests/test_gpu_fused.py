@@ -64,7 +64,10 @@ def test_fused_calls_match_separate_calls(cfg):
 
 
 @pytest.mark.parametrize("rows,H,V", [(65, 256, 2000), (1040, 256, 3000), (5, 384, 31000),
-                                      (122, 384, 5000), (11, 256, 4096)])
+                                      (122, 384, 5000), (11, 256, 4096),
+                                      # the LDS-DMA weight stream (non-temporal weights in
+                                      # the verify call, ordinary ones in medusa_heads)
+                                      (65, 256, 32000), (5, 384, 32000), (80, 128, 262144)])
 @pytest.mark.parametrize("mode", ["greedy", "typical"])
 def test_verify_logits_match_heads(rows, H, V, mode):
     """medusa_verify_logits writes the same logits as medusa_heads (one kernel
@@ -179,3 +182,65 @@ def test_split_heads_match_medusa_heads(b, H, V, K, dt):
     assert torch.equal(u1, u2)
     assert torch.equal(l1, l2)
     assert torch.equal(v1, v2)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "typical"])
+def test_weight_stream_partials_decide_as_the_logits(mode):
+    """Acceptance partials written by the LDS-DMA weight-stream GEMM (68 verify
+    rows over a 262144-entry vocabulary, past the 2^24 logits from which the
+    verify call keeps partials) give the same acceptance as folding the logits
+    rows (medusa_accept on the same logits), on a tree whose tokens are taken
+    from the rows' own ranking so that paths of every length occur."""
+    import numpy as np
+    from oracle import tree_plan
+    from speculative_decoding_heads_amd import medusa as M
+    from speculative_decoding_heads_amd.synth import normal
+    say("weight-stream partials", mode)
+    k, b, H, V = (4, 3), 4, 256, 262144
+    plan = tree_plan(k, None)
+    T, K = plan.T, len(k)
+    rows = b * T
+    assert rows <= 80 and rows * V >= 1 << 24
+    x = normal((rows, H), 611, 1.0, torch.bfloat16).to("cuda")
+    LM = normal((V, H), 612, 0.4, torch.bfloat16).to("cuda")
+    md = M.TYPICAL if mode == "typical" else M.GREEDY
+    logits = torch.empty(rows, V, device="cuda")
+    vws = M.workspace(M.medusa_verify_workspace(rows, H, V, M.BF16, md))
+    Tf = float(np.float32(0.7))
+    M.medusa_verify_logits(x, LM, logits, md, Tf, vws)
+    ref = torch.empty(rows, V, device="cuda")
+    M.medusa_lm_logits(x, LM, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, ref)
+    bl = logits.view(b, T, V).cpu().numpy()
+    tokens = np.zeros((b, T), dtype=np.int32)
+    for s in range(b):
+        for p in range(T):
+            kids = [c for c in range(1, T) if plan.parent[c] == p]
+            if kids:
+                order = np.argsort(-bl[s, p].astype(np.float64), kind="stable")
+                tokens[s, kids] = order[[s + 2 * j for j in range(len(kids))]]
+    tk = torch.from_numpy(tokens).to("cuda")
+    par = torch.tensor(plan.parent, dtype=torch.int32, device="cuda")
+    dep = torch.tensor(plan.depth, dtype=torch.int32, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    outs = []
+    for use_parts in (True, False):
+        nkv, d, P = 1, 64, 10
+        Kc = normal((b, nkv, P + T, d), 613, 1.0, torch.bfloat16).to("cuda")
+        Vc = normal((b, nkv, P + T, d), 614, 1.0, torch.bfloat16).to("cuda")
+        seq = torch.full((b,), P, **i32)
+        L, path = torch.empty(b, **i32), torch.empty(b, K + 1, **i32)
+        acc, bonus = torch.empty(b, K + 1, **i32), torch.empty(b, **i32)
+        ws = M.workspace(M.medusa_accept_workspace(b, T))
+        M.medusa_accept_compact(logits.view(b, T, V), tk, par, dep, K, md, Tf, 0.3, 0.09, 11, 3,
+                                L, path, acc, bonus, Kc, Vc, seq, ws,
+                                verify_ws=vws if use_parts else None)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (L, path, acc, bonus, Kc, Vc, seq)])
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+    Ls = outs[0][0].tolist()
+    if mode == "greedy":
+        # sequence s offers rank s as the first child: only sequence 0 accepts
+        assert Ls[0] == K and all(v == 0 for v in Ls[1:]), Ls

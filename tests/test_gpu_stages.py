@@ -131,6 +131,32 @@ def test_verify_rows_projection(rows, H, V):
     assert_rows_close(np64(out), ref, 2e-5 if dt == torch.bfloat16 else TOL_F32, "verify rows")
 
 
+@pytest.mark.parametrize("rows,H,V", [(1, 4096, 32000), (5, 4096, 32000), (17, 256, 32768),
+                                      (33, 512, 32000), (48, 8192, 32000), (65, 4096, 32000),
+                                      (80, 256, 128256)])
+def test_weight_stream_logits_both_walks(rows, H, V):
+    """The LDS-DMA weight-stream GEMM (at most 80 rows, vocabulary a multiple
+    of 128 and at least 30720): forward and backward K walks, and the verify
+    call's non-temporal weight reads, against the oracle's projection."""
+    say("weight stream", rows, H, V)
+    x = normal((rows, H), 7 * rows + 1, 1.0, torch.bfloat16)
+    LM = normal((V, H), 7 * rows + 2, 0.02, torch.bfloat16)
+    xd, LMd = x.to(DEV), LM.to(DEV)
+    ref = lm_project(np64(x), np64(LM))
+    ws = M.workspace(M.medusa_verify_workspace(rows, H, V, M.BF16, M.GREEDY))
+    outs = []
+    for rev in (0, 1, None):
+        out = torch.full((rows, V), float("nan"), dtype=torch.float32, device=DEV)
+        if rev is None:
+            M.medusa_verify_logits(xd, LMd, out, M.GREEDY, 1.0, ws)
+        else:
+            M.medusa_lm_logits(xd, LMd, out, reverse_k=rev)
+        torch.cuda.synchronize()
+        assert_rows_close(np64(out), ref, 2e-5, f"logits rev={rev}")
+        outs.append(out)
+    assert torch.equal(outs[0], outs[2])      # the cache hint changes no value
+
+
 # ------------------------------------------------------------------ top-k
 def _topk_run(logits, k, kmax, mode, temperature=0.7, seed=5, step=3):
     b, K1, V = logits.shape
