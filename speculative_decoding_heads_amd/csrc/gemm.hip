@@ -339,6 +339,108 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(const uint16_t* __restri
   epi.copy_base(n0, n0 + 16 * NB);
 }
 
+// ---------------------------------------------------------------- skinny bf16 by LDS DMA
+// gemm_skinny_bf16<2, 1> (32 weight rows per workgroup, 4 waves splitting K
+// in whole pairs of 128-wide chunks, the same chunk order and LDS reduction,
+// so the same outputs bit for bit) with the weights streamed global -> LDS by
+// DMA with the non-temporal hint (read once per step) into a 2-deep ring per
+// wave, and each wave's activation rows (at most 8 chunks: K <= 4096) held in
+// registers for the whole call.  The waves never wait on each other before
+// the reduction.  A ring slot holds the 32 rows of one chunk, row-major with
+// 16-byte pieces XOR-swizzled by row; each DMA issue covers four whole rows.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_dma_bf16(const uint16_t* __restrict__ X,
+                                                            int64_t ldx, int M,
+                                                            const uint16_t* __restrict__ W,
+                                                            int N, int Kd, Epi epi, int64_t bsx,
+                                                            int64_t bsw) {
+  constexpr int NB = 2, LDSROW = 128, MAXC = 8;
+  X += blockIdx.y * bsx;
+  W += blockIdx.y * bsw;
+  auto xsw = [](int r) { return (r & 3) | ((r & 4) << 1); };
+  __shared__ __attribute__((aligned(16))) uint16_t wring[4][2][16 * NB * LDSROW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NB;
+  const int nchunks = Kd >> 7;
+  const int npairs = nchunks >> 1;
+  const int p_begin = (npairs * wave) >> 2, p_end = (npairs * (wave + 1)) >> 2;
+  const int c0 = 2 * p_begin, nc = 2 * (p_end - p_begin);   // this wave's chunks, nc <= MAXC
+
+  // the activation fragments of all of this wave's chunks (indices clamped,
+  // so no load sits under a branch)
+  uint4 xr[MAXC][4];
+  const uint16_t* xp = X + (int64_t)min(r16, M - 1) * ldx + 32 * g4;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = min(c0 + min(j, max(nc - 1, 0)), nchunks - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xr[j][s] = ldg16(xp + (c << 7) + 8 * s);
+  }
+  const uint16_t* wsrc[4 * NB];
+#pragma unroll
+  for (int u = 0; u < 4 * NB; ++u) {
+    const int row = 4 * u + (lane >> 4);
+    wsrc[u] = W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * ((lane & 15) ^ xsw(row));
+  }
+  const uint32_t rl = lds_u32(&wring[wave][0][0]);
+  auto issue = [&](int c, int slot) {
+    const uint32_t base = rl + (uint32_t)(slot * 16 * NB * LDSROW * 2);
+#pragma unroll
+    for (int u = 0; u < 4 * NB; ++u)
+      dma16_nt(wsrc[u] + (c << 7), __builtin_amdgcn_readfirstlane(base + (uint32_t)(u * 1024)));
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = xsw(r16);
+  if (nc > 0) issue(c0, 0);
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    if (j < nc) {                                   // uniform
+      if (j + 1 < nc) {
+        // the slot chunk j+1 fills was read by chunk j-1: those LDS reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(c0 + j + 1, (j + 1) & 1);
+        vm_wait<4 * NB>();                          // chunk j landed (j+1 may be in flight)
+      } else {
+        vm_wait<0>();
+      }
+      const uint16_t* wb = &wring[wave][j & 1][0];
+      uint4 w[NB][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int row = 16 * nb + r16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          w[nb][s] = *reinterpret_cast<const uint4*>(wb + row * LDSROW + 8 * ((4 * g4 + s) ^ sw));
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(w[nb][s], xr[j][s], acc[nb]);
+    }
+  }
+
+  // cross-wave reduction of the 4 K-partials, as in gemm_skinny_bf16
+  __shared__ f32x4 red[4][NB][64];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[wave][nb][lane] = acc[nb];
+  __syncthreads();
+  for (int p = wave; p < NB; p += 4) {
+    f32x4 v = red[0][p][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      f32x4 t = red[w][p][lane];
+      v[0] += t[0]; v[1] += t[1]; v[2] += t[2]; v[3] += t[3];
+    }
+    epi.store4(r16, n0 + 16 * p + 4 * g4, v);
+  }
+  epi.copy_base(n0, n0 + 16 * NB);
+}
+
 // ---------------------------------------------------------------- tiled bf16
 // Tile index t -> (n tile, m tile) with all m tiles of one n tile adjacent on
 // one XCD (workgroups are dispatched round-robin over the 8 XCDs).
@@ -932,7 +1034,13 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
   // medusa_heads and medusa_verify_logits come from the same kernel
   const Bf16Plan p = plan_bf16(M, N, Kd, IsLogits<Epi>::value, !IsLogits<Epi>::value);
   if (p.kind == 0) {
-    // skinny: 4 waves split K, X (a few rows) read from L2
+    // skinny: 4 waves split K, X (a few rows) read from L2; with 32-row
+    // workgroups and K <= 4096 in whole chunk pairs, the weights by LDS DMA
+    if (p.snb == 2 && p.mb == 1 && (Kd % 256) == 0 && Kd <= 4096) {
+      hipLaunchKernelGGL((gemm_skinny_dma_bf16<Epi>), dim3(p.ntiles, batch), dim3(256), 0, st, X,
+                         ldx, M, W, N, Kd, epi, bsx, bsw);
+      return hipGetLastError();
+    }
     if (p.snb == 2)
       hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
                          X, ldx, M, W, N, Kd, epi, bsx, bsw);
