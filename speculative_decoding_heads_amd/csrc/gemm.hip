@@ -30,10 +30,12 @@
 //                 starts its K walk at its own chunk, so the workgroups do not
 //                 all read the same slice of X at once.  Tiles are mapped to
 //                 XCDs so that the M-tiles of one weight tile run on one XCD.
-//   gemm_dma    : the logits GEMMs of gemm_tiled's 8-wave shapes (at most 80
-//                 rows over a wide vocabulary: the heads' LM pass, the batch-1
-//                 verify rows): the same tile and MFMA order, with both
-//                 operands streamed global -> LDS by DMA (see below).
+//   gemm_dma    : gemm_tiled's 8-wave logits shapes (at most 80 rows over a
+//                 wide vocabulary: the heads' LM pass, the batch-1 verify
+//                 rows) and its 8/10-wave heads shapes of at most 16 rows: the
+//                 same tile and MFMA order, with both operands streamed global
+//                 -> LDS by DMA (see below).  gemm_skinny's 32-row
+//                 workgroups with K <= 4096 stream their weights by DMA too.
 //   gemm_ring   : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
@@ -606,7 +608,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_tiled_bf16(const uint16_t* _
 
 // ---------------------------------------------------------------- weight stream by LDS DMA
 // The logits GEMMs of at most 80 rows over a wide vocabulary (the heads' LM
-// pass, the batch-1 verify rows): the same tile as gemm_tiled_bf16 (BM =
+// pass, the batch-1 verify rows) and the heads' GEMM over wide weights (the
+// 70B layer's 40960 x 8192): the same tile as gemm_tiled_bf16 (BM =
 // 16*MB activation rows shared by NW waves of 16 weight rows each, the
 // rotated K walk, the same MFMA order, so the same logits bit for bit), but
 // both operands reach LDS by direct global->LDS loads through an NBUF-deep
@@ -728,6 +731,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_bf16(const uint16_t* __restr
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) epi.store4(m0 + 16 * mb + r16, n0 + 4 * g4, acc[mb]);
+  if (tm == 0) epi.copy_base(tn * BN, tn * BN + BN);
   if constexpr (HasParts<Epi>::value) {
     // row partials over this workgroup's BN columns, as in gemm_tiled_bf16
     __syncthreads();                        // every wave is past its last read of the ring
@@ -1074,6 +1078,19 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
 #undef RING
     return hipGetLastError();
   }
+  // heads over wide weights from at most 16 rows (8- or 10-wave workgroups;
+  // the weights are read once per step, non-temporally): the weight stream by
+  // LDS DMA
+  if constexpr (!IsLogits<Epi>::value)
+    if ((p.nw == 8 || p.nw == 10) && p.mb == 1 && batch == 1 && (N % (16 * p.nw)) == 0) {
+      if (p.nw == 8)
+        hipLaunchKernelGGL((gemm_dma_bf16<1, Epi, 8, 3>), dim3(p.ntiles), dim3(512), 0, st, X,
+                           ldx, M, W, N, Kd, 1, epi, rev, true);
+      else
+        hipLaunchKernelGGL((gemm_dma_bf16<1, Epi, 10, 3>), dim3(p.ntiles), dim3(640), 0, st, X,
+                           ldx, M, W, N, Kd, 1, epi, rev, true);
+      return hipGetLastError();
+    }
   // logits over a wide vocabulary from at most 80 rows in 8-wave workgroups:
   // the weight stream by LDS DMA (one problem per launch)
   if constexpr (IsLogits<Epi>::value)
