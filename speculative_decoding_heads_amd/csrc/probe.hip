@@ -6,49 +6,73 @@
 // weight streams' sizes to give the rate this part reaches for a read of
 // that many bytes, next to the 8 TB/s of the specification.
 //
-// Layout chosen by a sweep on MI355X (134 MB, 262 MB and 1 GiB, three
-// rotated buffers so the last-level cache cannot serve them): 512 workgroups
-// of 256 threads (two per CU), each thread four 16-byte loads in flight,
-// grid-stride.  Eight loads in flight, or four and eight workgroups per CU,
-// were 5-20% slower; a contiguous region per workgroup (as a GEMM workgroup
-// reads its weight rows) 2-5% slower at 134 MB.
+// The fastest plain read found on MI355X (134 MB, 262 MB and 1 GiB, three
+// rotated buffers so the last-level cache cannot serve them): direct
+// global->LDS loads with the non-temporal hint, 256 workgroups of 8 waves,
+// each wave two 1 KB loads per group (at most four in flight), grid-stride
+// over 1 KB units: 22.1 us, 40.7 us and 154 us.  Loads into registers (four
+// 16-byte loads in flight per thread, 512 workgroups of 256 threads) took
+// 24.3, 45.8 and 178 us; LDS DMA without the hint 23.5, 45.4 and 179 us;
+// four or eight loads per group, or 512 workgroups, 2-15% longer.
+// Each lane folds the 16 bytes it brought in by XOR (read back from LDS) and
+// writes its fold to sink only when it equals the caller's `never`, so every
+// word is seen by some lane and nothing can be dropped; the last partial
+// 1 KB unit is read into registers by the first workgroup.
 
 #include "common.h"
 #include "kernels.h"
 
 namespace medusa {
 
-constexpr int kReadThreads = 256;
-constexpr int kReadBlocks = 512;
-constexpr int kReadUnroll = 4;
+constexpr int kReadWaves = 8;
+constexpr int kReadBlocks = 256;
+constexpr int kReadGroup = 2;          // 1 KB loads per wave and group
 
-// Each thread folds the words it loaded by XOR and writes its fold to sink
-// only when it equals the caller's `never`, so the loads cannot be dropped
-// (for a value no fold takes, nothing is written).
-__global__ __launch_bounds__(kReadThreads) void stream_read(const uint4* __restrict__ p, size_t n16,
-                                                            uint32_t never,
-                                                            uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kReadThreads;
-  size_t i = blockIdx.x * (size_t)kReadThreads + threadIdx.x;
+__global__ __launch_bounds__(64 * kReadWaves) void stream_read(const uint8_t* __restrict__ p,
+                                                               size_t bytes, uint32_t never,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint4 lds[kReadWaves][2][kReadGroup][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t units = bytes >> 10;
+  const size_t tw = (size_t)gridDim.x * kReadWaves;
+  size_t u = (size_t)blockIdx.x * kReadWaves + wave;
   uint32_t acc = 0;
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
-    uint4 v[kReadUnroll];
+  auto fold = [&](const uint4& v) { acc ^= v.x ^ v.y ^ v.z ^ v.w; };
+  int slot = 0;
+  for (; u + (size_t)(kReadGroup - 1) * tw < units; u += (size_t)kReadGroup * tw) {
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = p[i + u * stride];
+    for (int j = 0; j < kReadGroup; ++j)
+      dma16_nt(p + (u + (size_t)j * tw) * 1024 + 16 * lane,
+               __builtin_amdgcn_readfirstlane(lds_u32(&lds[wave][slot][j][0])));
+    // the previous group (the other slot) has landed; fold it
+    vm_wait<kReadGroup>();
+    if (u >= (size_t)kReadGroup * tw) {
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      for (int j = 0; j < kReadGroup; ++j) fold(lds[wave][slot ^ 1][j][lane]);
+    }
+    // the other slot is refilled next group only after these reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    slot ^= 1;
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  vm_wait<0>();
+  if (u >= (size_t)kReadGroup * tw) {
+#pragma unroll
+    for (int j = 0; j < kReadGroup; ++j) fold(lds[wave][slot ^ 1][j][lane]);
+  }
+  for (; u < units; u += tw) fold(*reinterpret_cast<const uint4*>(p + u * 1024 + 16 * lane));
+  if (blockIdx.x == 0) {
+    const size_t tail = bytes & 1023;
+    for (size_t o = 16 * (size_t)threadIdx.x; o < tail; o += 16 * 64 * kReadWaves)
+      fold(*reinterpret_cast<const uint4*>(p + (units << 10) + o));
   }
   if (acc == never) sink[0] = acc;
 }
 
 hipError_t run_stream_read(const void* buf, size_t bytes, uint32_t never, uint32_t* sink,
                            hipStream_t st) {
-  hipLaunchKernelGGL(stream_read, dim3(kReadBlocks), dim3(kReadThreads), 0, st,
-                     static_cast<const uint4*>(buf), bytes / 16, never, sink);
+  hipLaunchKernelGGL(stream_read, dim3(kReadBlocks), dim3(64 * kReadWaves), 0, st,
+                     static_cast<const uint8_t*>(buf), bytes, never, sink);
   return hipGetLastError();
 }
 
