@@ -35,7 +35,8 @@
 //                 rows) and its 8/10-wave heads shapes of at most 16 rows: the
 //                 same tile and MFMA order, with both operands streamed global
 //                 -> LDS by DMA (see below).  gemm_skinny's 32-row
-//                 workgroups with K <= 4096 stream their weights by DMA too.
+//                 workgroups with K <= 4096 stream their weights by DMA too,
+//                 its 16-row ones both operands.
 //   gemm_ring   : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
@@ -441,6 +442,104 @@ __global__ __launch_bounds__(256) void gemm_skinny_dma_bf16(const uint16_t* __re
     epi.store4(r16, n0 + 16 * p + 4 * g4, v);
   }
   epi.copy_base(n0, n0 + 16 * NB);
+}
+
+// gemm_skinny_bf16<1, MB> (16 weight rows per workgroup: the single-head
+// GEMMs, N = H) with both operands streamed global -> LDS by DMA through a
+// 2-deep ring per wave: K may be long (11008), so the activation rows are
+// not held in registers.  The waves split K in whole pairs of 128-wide chunks
+// (wave 0 also takes an odd last chunk), in the same order as the register
+// kernel, with the same MFMA order and reduction: the same outputs bit for
+// bit.  A slot holds the chunk's 16 weight rows and then its 16 MB activation
+// rows (clamped to M - 1), row-major, 16-byte pieces XOR-swizzled by row;
+// weights with the non-temporal hint (read once), activations without.
+template <int MB, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny1_dma_bf16(const uint16_t* __restrict__ X,
+                                                             int64_t ldx, int M,
+                                                             const uint16_t* __restrict__ W,
+                                                             int N, int Kd, Epi epi, int64_t bsx,
+                                                             int64_t bsw) {
+  constexpr int LDSROW = 128, ROWS = 16 + 16 * MB, NU = ROWS / 4;   // 1 KB units per chunk
+  X += blockIdx.y * bsx;
+  W += blockIdx.y * bsw;
+  auto xsw = [](int r) { return (r & 3) | ((r & 4) << 1); };
+  __shared__ __attribute__((aligned(16))) uint16_t wring[4][2][ROWS * LDSROW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int nchunks = Kd >> 7;
+  const int npairs = nchunks >> 1;
+  const int p_begin = (npairs * wave) >> 2, p_end = (npairs * (wave + 1)) >> 2;
+  const int c0 = 2 * p_begin;
+  const bool odd = (nchunks & 1) && wave == 0;
+  const int nc = 2 * (p_end - p_begin) + (odd ? 1 : 0);   // this wave's chunks
+  auto chunk = [&](int j) { return j < 2 * (p_end - p_begin) ? c0 + j : nchunks - 1; };
+
+  // unit u: rows 4u..4u+3 of the slot (weights first, then activations)
+  const uint16_t* src[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int row = 4 * u + (lane >> 4);
+    const int part = (lane & 15) ^ xsw(row);
+    src[u] = row < 16 ? W + (int64_t)min(n0 + row, N - 1) * Kd + 8 * part
+                      : X + (int64_t)min(row - 16, M - 1) * ldx + 8 * part;
+  }
+  const uint32_t rl = lds_u32(&wring[wave][0][0]);
+  auto issue = [&](int c, int slot) {
+    const uint32_t base = rl + (uint32_t)(slot * ROWS * LDSROW * 2);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const uint32_t l = __builtin_amdgcn_readfirstlane(base + (uint32_t)(u * 1024));
+      if (u < 4) dma16_nt(src[u] + (c << 7), l);
+      else dma16(src[u] + (c << 7), l);
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = xsw(r16);
+  if (nc > 0) issue(chunk(0), 0);
+  for (int j = 0; j < nc; ++j) {
+    if (j + 1 < nc) {
+      // the slot chunk j+1 fills was read by chunk j-1: those LDS reads are done
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(chunk(j + 1), (j + 1) & 1);
+      vm_wait<NU>();                                 // chunk j landed (j+1 may be in flight)
+    } else {
+      vm_wait<0>();
+    }
+    const uint16_t* sb = &wring[wave][j & 1][0];
+    uint4 w[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      w[s] = *reinterpret_cast<const uint4*>(sb + r16 * LDSROW + 8 * ((4 * g4 + s) ^ sw));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(
+            sb + (16 + 16 * mb + r16) * LDSROW + 8 * ((4 * g4 + s) ^ sw));
+        acc[mb] = mfma16x16x32(w[s], xv, acc[mb]);
+      }
+  }
+
+  // cross-wave reduction of the 4 K-partials, as in gemm_skinny_bf16
+  __shared__ f32x4 red[4][MB][64];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+  __syncthreads();
+  for (int p = wave; p < MB; p += 4) {
+    f32x4 v = red[0][p][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      f32x4 t = red[w][p][lane];
+      v[0] += t[0]; v[1] += t[1]; v[2] += t[2]; v[3] += t[3];
+    }
+    epi.store4(16 * p + r16, n0 + 4 * g4, v);
+  }
+  epi.copy_base(n0, n0 + 16);
 }
 
 // ---------------------------------------------------------------- tiled bf16
@@ -1043,6 +1142,16 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
     if (p.snb == 2 && p.mb == 1 && (Kd % 256) == 0 && Kd <= 4096) {
       hipLaunchKernelGGL((gemm_skinny_dma_bf16<Epi>), dim3(p.ntiles, batch), dim3(256), 0, st, X,
                          ldx, M, W, N, Kd, epi, bsx, bsw);
+      return hipGetLastError();
+    }
+    // 16-row workgroups (single-head GEMMs): both operands by LDS DMA
+    if (p.snb == 1 && (Kd % 128) == 0) {
+      if (p.mb == 1)
+        hipLaunchKernelGGL((gemm_skinny1_dma_bf16<1, Epi>), dim3(p.ntiles, batch), dim3(256), 0,
+                           st, X, ldx, M, W, N, Kd, epi, bsx, bsw);
+      else
+        hipLaunchKernelGGL((gemm_skinny1_dma_bf16<2, Epi>), dim3(p.ntiles, batch), dim3(256), 0,
+                           st, X, ldx, M, W, N, Kd, epi, bsx, bsw);
       return hipGetLastError();
     }
     if (p.snb == 2)
