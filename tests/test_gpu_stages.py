@@ -34,12 +34,16 @@ HEAD_CASES = [
     (1, 128, 1000, 4, "bf16"),     # skinny 1-block; one 16-row block, ragged vocab tile
     (3, 256, 4093, 2, "bf16"),     # V % 4 != 0: scalar logit stores
     (17, 384, 2048, 1, "bf16"),    # N = H < 8192, 17 rows: 16-row skinny workgroups with
-                                   # two row blocks; 3 K-chunks (odd); 34 LM rows
+                                   # two row blocks, both operands by LDS DMA; 3 K-chunks
+                                   # (odd: wave 0 takes the last); 34 LM rows
     (16, 256, 3000, 4, "bf16"),    # N = 1024, 16 rows: skinny, one row block; 80 LM rows
     (32, 256, 1000, 1, "bf16"),    # N = H, 32 rows: the last row count on skinny workgroups
     (33, 256, 1000, 1, "bf16"),    # N = H, 33 rows: the first on the tiled kernel
     (40, 256, 1000, 4, "bf16"),    # 200 LM rows: tiled kernel, ragged M and N tiles
-    (3, 2048, 1000, 16, "bf16"),   # 32768 head rows: 8-wave tiled, rotated K walk
+    (3, 2048, 1000, 16, "bf16"),   # 32768 head rows: 8-wave LDS-DMA weight stream, rotated K walk
+    (8, 8192, 1000, 5, "bf16"),    # 40960 x 8192 head rows: the 10-wave LDS-DMA weight stream
+    (1, 4096, 1000, 4, "bf16"),    # the 7B batch-1 heads: skinny, weights by LDS DMA, X in registers
+    (16, 4096, 1000, 4, "bf16"),   # 16 rows, K = 4096: the same kernel at its row limit
     (1, 256, 4096, 3, "f32"),      # tiny fp32 workload shape
     (5, 100, 777, 2, "f32"),
 ]
