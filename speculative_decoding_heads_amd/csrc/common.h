@@ -43,16 +43,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f3
 
 // ---- loads ----------------------------------------------------------------------
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-// Streaming (single-use) load: non-temporal hint so it does not evict reused lines.
-__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  uint4 r;
-  r.x = __builtin_nontemporal_load(&q->x);
-  r.y = __builtin_nontemporal_load(&q->y);
-  r.z = __builtin_nontemporal_load(&q->z);
-  r.w = __builtin_nontemporal_load(&q->w);
-  return r;
-}
 
 // LDS DMA (gfx950 global_load_lds_dwordx4): each lane's 16 bytes from its own
 // global address land at LDS byte m0 + 16 * lane.  The compiler does not see

@@ -15,12 +15,16 @@
 // are the MFMA "A" rows, X rows the "B" columns, so each lane ends up with 4
 // consecutive n of one output row (one 16-byte store of logits).
 //
-// Four bf16 kernels:
-//   gemm_skinny : M <= 16 with fewer than 30720 weight rows.  HBM-bound weight
-//                 stream.  A workgroup owns 16*NB weight rows; its 4 waves
-//                 split K and reduce through LDS.  Both operands go global ->
-//                 registers (X is tiny and stays in L2); each lane loads 64
-//                 contiguous bytes per row per step.
+// bf16 kernels:
+//   gemm_skinny : M <= 16 with fewer than 30720 weight rows (M <= 32 for a
+//                 single head, N = H).  HBM-bound weight stream.  A workgroup
+//                 owns 16*NB weight rows; its 4 waves split K and reduce
+//                 through LDS.  With 32 rows and K > 4096 both operands go
+//                 global -> registers (X is tiny and stays in L2; each lane
+//                 loads 64 contiguous bytes per row per step); with K <= 4096
+//                 the weights stream by LDS DMA and X sits in registers
+//                 (gemm_skinny_dma); with 16 rows both operands stream by LDS
+//                 DMA (gemm_skinny1_dma).
 //   gemm_tiled  : the other M <= 80 cases (and heads with larger M).  A
 //                 workgroup of 8 waves (4 when there are too few weight rows to
 //                 give every CU a 128-row tile) owns BM = 16*MB activation rows
@@ -34,9 +38,7 @@
 //                 wide vocabulary: the heads' LM pass, the batch-1 verify
 //                 rows) and its 8/10-wave heads shapes of at most 16 rows: the
 //                 same tile and MFMA order, with both operands streamed global
-//                 -> LDS by DMA (see below).  gemm_skinny's 32-row
-//                 workgroups with K <= 4096 stream their weights by DMA too,
-//                 its 16-row ones both operands.
+//                 -> LDS by DMA (see below).
 //   gemm_ring   : M > 80, MFMA-bound (see below).
 // One f32 kernel (tiny fp32 workload): one wave per weight row.
 
@@ -1145,7 +1147,8 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
       return hipGetLastError();
     }
     // 16-row workgroups (single-head GEMMs): both operands by LDS DMA
-    if (p.snb == 1 && (Kd % 128) == 0) {
+    // (every bf16 entry point requires K % 128 == 0)
+    if (p.snb == 1) {
       if (p.mb == 1)
         hipLaunchKernelGGL((gemm_skinny1_dma_bf16<1, Epi>), dim3(p.ntiles, batch), dim3(256), 0,
                            st, X, ldx, M, W, N, Kd, epi, bsx, bsw);
@@ -1154,15 +1157,9 @@ static hipError_t launch_bf16(const uint16_t* X, int64_t ldx, int M, const uint1
                            st, X, ldx, M, W, N, Kd, epi, bsx, bsw);
       return hipGetLastError();
     }
-    if (p.snb == 2)
-      hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
-                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
-    else if (p.mb == 1)
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
-                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
-    else
-      hipLaunchKernelGGL((gemm_skinny_bf16<1, 2, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st,
-                         X, ldx, M, W, N, Kd, epi, bsx, bsw);
+    // 32-row workgroups with K > 4096: the weights into registers
+    hipLaunchKernelGGL((gemm_skinny_bf16<2, 1, Epi>), dim3(p.ntiles, batch), dim3(256), 0, st, X,
+                       ldx, M, W, N, Kd, epi, bsx, bsw);
     return hipGetLastError();
   }
   if constexpr (IsLogits<Epi>::value) if (p.kind == 2) {
