@@ -44,6 +44,7 @@ HEAD_CASES = [
     (8, 8192, 1000, 5, "bf16"),    # 40960 x 8192 head rows: the 10-wave LDS-DMA weight stream
     (1, 4096, 1000, 4, "bf16"),    # the 7B batch-1 heads: skinny, weights by LDS DMA, X in registers
     (16, 4096, 1000, 4, "bf16"),   # 16 rows, K = 4096: the same kernel at its row limit
+    (2, 512, 1000, 16, "bf16"),    # the same kernel with 4 K-chunks: waves 0 and 2 get none
     (1, 256, 4096, 3, "f32"),      # tiny fp32 workload shape
     (5, 100, 777, 2, "f32"),
 ]
