@@ -348,6 +348,13 @@ int medusa_accept_compact(const float* base_logits, const int32_t* tokens, const
  *   ws: medusa_verify_workspace(rows, H, V, dtype, mode) bytes, 16-byte
  *       aligned, device, caller-owned; contents are opaque.
  * logits are bit-identical to medusa_heads.  Errors as medusa_heads.
+ * Cache use (no effect on any value): this call, the step's last pass over
+ * LM, reads LM with the non-temporal hint where the weight-stream kernel
+ * runs (at most 80 rows over a vocabulary that is a multiple of 128 and at
+ * least 30720), and stores the logits non-temporally when it keeps partials;
+ * medusa_heads and medusa_lm_logits read LM without the hint, so a verify
+ * call that follows them on the same LM finds much of it in the
+ * last-level cache.
  * ------------------------------------------------------------------------- */
 size_t medusa_verify_workspace(int64_t rows, int32_t H, int32_t V, int32_t dtype, int32_t mode);
 int medusa_verify_logits(const void* x, int64_t rows, int32_t H, const void* LM, int32_t V,
